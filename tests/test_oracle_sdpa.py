@@ -1,0 +1,211 @@
+"""Pins for the fp64 attention oracle (CPU only).
+
+Each test checks the oracle against something other than itself:
+
+* closed forms -- the causal first row, zero queries (uniform attention), one key;
+* invariants -- softmax rows sum to one, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i;
+* an independent formula -- log-sum-exp without max subtraction;
+* brute force -- central finite differences of L = sum(dO * O), with dropout;
+* a library routine -- PyTorch's own CPU float64 attention and autograd.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import philox_ref, sdpa_ref
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _case(B, H, Sq, Sk, E, seed=0, kscale=1.0):
+    q = _rand((B, H, Sq, E), seed)
+    k = _rand((B, H, Sk, E), seed + 1, kscale)
+    v = _rand((B, H, Sk, E), seed + 2)
+    do = _rand((B, H, Sq, E), seed + 3)
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    q, k, v, _ = _case(1, 1, 37, 53, 16, seed=1, kscale=3.0)
+    s = sdpa_ref.resolve_scale(None, 16)
+    valid = sdpa_ref.valid_mask(37, 53, causal)
+    _, _, P = sdpa_ref.head_forward(q[0, 0], k[0, 0], v[0, 0], s, valid, np.ones((37, 53)))
+    assert np.allclose(P.sum(axis=1), 1.0, atol=1e-12, rtol=0)
+    assert (P[~valid] == 0).all()
+
+
+def test_default_scale():
+    assert sdpa_ref.resolve_scale(None, 64) == 0.125
+    assert sdpa_ref.resolve_scale(float("nan"), 128) == 1 / math.sqrt(128)
+    assert sdpa_ref.resolve_scale(0.3, 64) == 0.3
+
+
+@pytest.mark.parametrize("p", [0.0, 0.25])
+def test_causal_first_row(p):
+    # Row 0 attends to key 0 only: O_0 = v_0 * M_00 and LSE_0 = s * q_0 . k_0.
+    B, H, Sq, Sk, E = 2, 3, 9, 11, 8
+    q, k, v, _ = _case(B, H, Sq, Sk, E, seed=2)
+    seed, off = 1234, 77
+    out, lse = sdpa_ref.fwd(q, k, v, p, True, None, seed, off)
+    s = 1 / math.sqrt(E)
+    keep = philox_ref.keep_mask(seed, off, p, B, H, Sq, Sk) if p > 0 else np.ones((B, H, Sq, Sk))
+    for b in range(B):
+        for h in range(H):
+            m = keep[b, h, 0, 0] / (1 - p) if p > 0 else 1.0
+            assert np.allclose(out[b, h, 0], v[b, h, 0] * m, atol=1e-14)
+            assert math.isclose(lse[b, h, 0], s * float(q[b, h, 0] @ k[b, h, 0]), abs_tol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_equals_direct_log_sum_exp(causal):
+    B, H, Sq, Sk, E = 1, 2, 33, 40, 64
+    q, k, v, _ = _case(B, H, Sq, Sk, E, seed=3, kscale=3.0)
+    _, lse = sdpa_ref.fwd(q, k, v, 0.0, causal)
+    s = 1 / math.sqrt(E)
+    for h in range(H):
+        S = s * q[0, h] @ k[0, h].T
+        for i in range(Sq):
+            n = i + 1 if causal else Sk
+            direct = math.log(sum(math.exp(S[i, j]) for j in range(n)))
+            assert math.isclose(lse[0, h, i], direct, rel_tol=0, abs_tol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.3])
+def test_zero_queries_give_uniform_attention(causal, p):
+    # Q = 0 makes every valid score 0: P is uniform over the n_i valid keys, so
+    # O_i = (1/n_i) sum_{valid j} M_ij v_j and LSE_i = ln(n_i).
+    B, H, Sq, Sk, E = 2, 2, 13, 10, 8
+    _, k, v, _ = _case(B, H, Sq, Sk, E, seed=4)
+    q = np.zeros((B, H, Sq, E))
+    seed, off = 42, 5
+    out, lse = sdpa_ref.fwd(q, k, v, p, causal, None, seed, off)
+    keep = philox_ref.keep_mask(seed, off, p, B, H, Sq, Sk)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Sq):
+                n = min(i + 1, Sk) if causal else Sk
+                w = keep[b, h, i, :n] / (1 - p) if p > 0 else np.ones(n)
+                expect = (w[:, None] * v[b, h, :n]).sum(axis=0) / n
+                assert np.allclose(out[b, h, i], expect, atol=1e-13)
+                assert math.isclose(lse[b, h, i], math.log(n), abs_tol=1e-13)
+
+
+def test_single_key():
+    # Sk = 1: every row copies v_0; dQ = dK = 0; dV = sum_i dO_i.
+    B, H, Sq, E = 1, 2, 7, 8
+    q, k, v, do = _case(B, H, Sq, 1, E, seed=5)
+    for causal in (False, True):
+        out, _ = sdpa_ref.fwd(q, k, v, 0.0, causal)
+        assert np.allclose(out, np.broadcast_to(v, out.shape), atol=1e-14)
+        dq, dk, dv = sdpa_ref.bwd(do, q, k, v, 0.0, causal)
+        assert np.allclose(dq, 0, atol=1e-13) and np.allclose(dk, 0, atol=1e-13)
+        assert np.allclose(dv[:, :, 0], do.sum(axis=2), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_invariants(causal):
+    B, H, Sq, Sk, E = 1, 2, 24, 31, 16
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=6)
+    out, _ = sdpa_ref.fwd(q, k, v, 0.0, causal)
+    dq, dk, dv = sdpa_ref.bwd(do, q, k, v, 0.0, causal)
+    # Rows of dS sum to zero, so sum_j dK_j = s * sum_i (sum_j dS_ij) q_i = 0.
+    assert np.allclose(dk.sum(axis=2), 0, atol=1e-12)
+    # With p = 0 the columns of P^T sum to one over each row i.
+    assert np.allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+    # D = sum_j P dP equals rowsum(dO * O).
+    s = 1 / math.sqrt(E)
+    valid = sdpa_ref.valid_mask(Sq, Sk, causal)
+    for h in range(H):
+        *_, D = sdpa_ref.head_backward(do[0, h], q[0, h], k[0, h], v[0, h], s, valid,
+                                       np.ones((Sq, Sk)))
+        assert np.allclose(D, (do[0, h] * out[0, h]).sum(axis=1), atol=1e-12)
+
+
+@pytest.mark.parametrize("Sq", [1, 3, 5])
+@pytest.mark.parametrize("Sk", [1, 4, 7])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.3])
+def test_finite_differences(Sq, Sk, causal, p):
+    B, H, E = 1, 2, 4
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=10 + Sq * 7 + Sk)
+    seed, off = 2024, 3
+
+    def loss(qq, kk, vv):
+        out, _ = sdpa_ref.fwd(qq, kk, vv, p, causal, None, seed, off)
+        return float((do * out).sum())
+
+    dq, dk, dv = sdpa_ref.bwd(do, q, k, v, p, causal, seed, off)
+    step = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += step
+            xm[idx] -= step
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            fd[idx] = (loss(args_p["q"], args_p["k"], args_p["v"])
+                       - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * step)
+        err = np.linalg.norm(fd - g) / max(np.linalg.norm(g), 1e-30)
+        assert err <= 1e-6 or np.abs(fd - g).max() < 1e-8, (name, err)
+
+
+def _torch_attention(q, k, v, do, causal, scale):
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                           scale=scale)
+    out.backward(torch.tensor(do, dtype=torch.float64))
+    return out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("shape,causal,kscale", [
+    ((1, 2, 128, 128, 64), True, 1.0),     # tiny causal workload's shape
+    ((1, 2, 128, 128, 64), False, 3.0),    # wide-score workload's shape
+    ((1, 2, 64, 128, 128), False, 1.0),    # reduced long cross-attention, head dim 128
+    ((1, 1, 48, 80, 32), True, 1.0),       # causal with Sq < Sk (top-left)
+    ((2, 1, 80, 48, 32), True, 1.0),       # causal with Sq > Sk (top-left)
+])
+def test_against_torch_cpu_float64(shape, causal, kscale):
+    B, H, Sq, Sk, E = shape
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=20, kscale=kscale)
+    s = 1 / math.sqrt(E)
+    out, _ = sdpa_ref.fwd(q, k, v, 0.0, causal)
+    dq, dk, dv = sdpa_ref.bwd(do, q, k, v, 0.0, causal)
+    t_out, t_dq, t_dk, t_dv = _torch_attention(q, k, v, do, causal, s)
+    for a, b in ((out, t_out), (dq, t_dq), (dk, t_dk), (dv, t_dv)):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-11)
+
+
+def test_workload_inputs_feed_the_oracle():
+    # The bf16 workload tensors are widened exactly; BSHE holds the BHSE values.
+    w = workloads.WORKLOADS["tiny_bshe_wide_scores"]
+    q, k, v, do = workloads.make_inputs(w)
+    assert q.dtype == torch.bfloat16 and q.stride()[-1] == 1
+    assert q.stride(2) == w.H * w.E  # memory [b, s, h, e]
+    q2, k2, v2, do2 = workloads.draw(w.B, w.H, w.Sq, w.Sk, w.E, w.gen_seed, w.k_scale, "BHSE")
+    for a, b in ((q, q2), (k, k2), (v, v2), (do, do2)):
+        assert torch.equal(a, b)
+    out_a, lse_a = sdpa_ref.fwd(q, k, v, 0.0, w.causal)
+    out_b, lse_b = sdpa_ref.fwd(q2, k2, v2, 0.0, w.causal)
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+
+
+def test_rows_and_heads_subsets_match_full():
+    B, H, Sq, Sk, E = 2, 2, 21, 19, 8
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=30)
+    for p, causal in ((0.0, True), (0.2, True), (0.2, False)):
+        out, lse = sdpa_ref.fwd(q, k, v, p, causal, None, 9, 11)
+        rows = [0, 5, 20]
+        o_r, l_r = sdpa_ref.fwd_rows(q, k, v, 1, 0, rows, p, causal, None, 9, 11)
+        assert np.array_equal(o_r, out[1, 0, rows]) and np.array_equal(l_r, lse[1, 0, rows])
+        out_h, _ = sdpa_ref.fwd(q, k, v, p, causal, None, 9, 11, heads=[(1, 1)])
+        assert np.array_equal(out_h[1, 1], out[1, 1]) and np.isnan(out_h[0, 0]).all()
