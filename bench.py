@@ -1,0 +1,239 @@
+"""Benchmark of the fused SDPA hot path on one MI355X.
+
+A step is one forward plus one backward (every kernel of the path) over the
+b2 h12 s1024 d64 causal bf16 workload (the shape of the nvFuser test
+``test_sdpa_loop_split``), with inputs resident in HBM before timing starts.
+
+Prints ONE JSON line:
+  value         whole-step TFLOP/s, counted FLOPs (forward 4*B*H*Sq*Sk*E, halved
+                when causal; backward 2.5x forward) over the timed step time
+  fwd / bwd     the same for forward-only and backward-only timed loops, and
+                their fraction of the bf16 dense MFMA peak
+  kernels       average duration of each kernel, from HIP events recorded by the
+                library around its own launches on its stream
+  roofline      the dominant kernel against its roofline
+  cpu_baseline  the fp64 CPU oracle on the host cores (a reported baseline)
+
+Options: --steps K --warmup W --gpus N (N must be 1), --no-cpu-baseline,
+--workload NAME, --copy-bytes N (time a plain device copy of N bytes instead,
+for calibrating hardware byte counters).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "fwd / bwd TFLOP/s and % bf16 MFMA peak at b2 h12 s1024 d64 causal"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b2_h12_s1024_d64_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time spent on the oracle baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def copy_calibration(nbytes: int, steps: int):
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes": nbytes, "launches": steps, "s_per_copy": dt,
+                      "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
+def timed_loop(fn, steps: int):
+    import torch
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps  # ms
+
+
+def cpu_baseline(w, q, k, v, do, min_seconds: float):
+    """Oracle forward + backward on whole heads until min_seconds of CPU time."""
+    from oracle import sdpa_ref
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
+    except Exception:  # pragma: no cover
+        threads, blas = int(os.environ.get("OMP_NUM_THREADS", "1")), "unknown"
+    qc, kc, vc, dc = (t.cpu() for t in (q, k, v, do))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    per_head = w.fwd_flops() / len(heads) * 3.5  # forward + backward counted FLOPs
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while True:
+        b, h = heads[done % len(heads)]
+        sdpa_ref.fwd(qc, kc, vc, w.dropout_p, w.causal, heads=[(b, h)])
+        sdpa_ref.bwd(dc, qc, kc, vc, w.dropout_p, w.causal, heads=[(b, h)])
+        done += 1
+        flops += per_head
+        if time.perf_counter() - t0 >= min_seconds and done >= 2:
+            break
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"{done} whole heads (of {len(heads)}) of the same workload, fp64 numpy "
+                      f"forward + backward, {dt:.1f} s wall; BLAS {blas} with {threads} threads "
+                      f"on {cores} visible cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: heads shard across GPUs with no exchange, so one GPU's share is "
+              "the same kernel on fewer heads.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import scaled_dot_product_14_amd as sdpa
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"workload {w}")
+    q, k, v, do = workloads.make_inputs(w, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(sdpa.sdpa_bwd_workspace_size(w.B, w.H, w.Sq, w.Sk, w.E), dtype=torch.uint8,
+                     device="cuda")
+    sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset)
+    state = {}
+
+    def fwd():
+        _, _, s, o = sdpa.sdpa_fwd(q, k, v, w.dropout_p, w.causal, None, out=out, lse=lse)
+        state["so"] = (s, o)
+
+    def bwd():
+        s, o = state["so"]
+        sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq, dk=dk,
+                      dv=dv, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warm-up done")
+
+    ms_step = timed_loop(step, args.steps)
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step")
+    ms_fwd = timed_loop(fwd, args.steps)
+    ms_bwd = timed_loop(bwd, args.steps)
+    log(f"fwd {ms_fwd * 1e3:.2f} us, bwd {ms_bwd * 1e3:.2f} us")
+
+    # Per-kernel durations: events recorded by the library around each launch.
+    names = {sdpa.KERNEL_FWD: "fwd", sdpa.KERNEL_BWD_PRE: "bwd_pre",
+             sdpa.KERNEL_BWD_MAIN: "bwd_main", sdpa.KERNEL_BWD_DQ: "bwd_dq"}
+    for kind in names:
+        sdpa.sdpa_profile_read(kind)
+    sdpa.sdpa_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    sdpa.sdpa_profile_enable(False)
+    kern = {}
+    for kind, name in names.items():
+        tot, n = sdpa.sdpa_profile_read(kind)
+        kern[name] = {"avg_us": tot / max(n, 1) * 1e3, "launches": n}
+    log(f"kernel averages (us): { {k_: round(v_['avg_us'], 2) for k_, v_ in kern.items()} }")
+
+    f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
+    rows = w.B * w.H * w.Sq
+    pre_bytes = rows * w.E * 2 * 2 + rows * 4 + rows * w.E * 4  # read dO, O; write D, zero dQ_acc
+    dq_bytes = rows * w.E * 4 + rows * w.E * 2
+    kern["fwd"].update(algorithmic_tflop=f_fwd / 1e12)
+    kern["bwd_main"].update(algorithmic_tflop=f_bwd / 1e12)
+    kern["bwd_pre"].update(algorithmic_bytes=pre_bytes)
+    kern["bwd_dq"].update(algorithmic_bytes=dq_bytes)
+    for name in ("fwd", "bwd_main"):
+        kk = kern[name]
+        kk["tflops"] = kk["algorithmic_tflop"] / (kk["avg_us"] * 1e-6)
+        kk["frac_peak"] = kk["tflops"] / PEAK_BF16_TFLOPS
+    for name in ("bwd_pre", "bwd_dq"):
+        kk = kern[name]
+        kk["GBps"] = kk["algorithmic_bytes"] / (kk["avg_us"] * 1e-6) / 1e9
+        kk["frac_hbm"] = kk["GBps"] / PEAK_HBM_GBS
+    dominant = max(kern, key=lambda n: kern[n]["avg_us"])
+    dk_ = kern[dominant]
+    if "tflops" in dk_:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
+                "traffic": None}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": dk_["GBps"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dk_["frac_hbm"], "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "E": w.E,
+                   "layout": w.layout, "causal": w.causal, "dropout_p": w.dropout_p,
+                   "cache": "warm (same buffers every step)"},
+        "fwd": {"tflops": f_fwd / (ms_fwd * 1e-3) / 1e12, "us": ms_fwd * 1e3,
+                "frac_peak": f_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "bwd": {"tflops": f_bwd / (ms_bwd * 1e-3) / 1e12, "us": ms_bwd * 1e3,
+                "frac_peak": f_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "kernels": kern,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, do, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * sdpa14 -- fused scaled-dot-product attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libsdpa14.so.  Plain pointers and sizes only; no PyTorch types.
+ *
+ * The two compute calls follow the forward/backward statement of the nvFuser
+ * PR "DID loop split for SDPA" (test test_sdpa_loop_split):
+ *
+ *   attn, log_sumexp, seed, offset = sdpfa_fwd(q, k, v, dropout_p, is_causal, scale)
+ *   q_grad, k_grad, v_grad = sdpfa_bwd(out_grad, q, k, v, attn, log_sumexp,
+ *                                      dropout_p, is_causal, seed, offset, scale)
+ *
+ * What is computed: O = dropout(softmax(Q K^T * scale + causal mask)) V, the
+ * definition of scaled-dot-product attention (forum thread
+ * "Scaled_dot_product_attention", opening question; nvFuser issue 2278).
+ *
+ *   - scale: NaN selects 1/sqrt(E).  Otherwise it must be finite and > 0.
+ *   - causal: key j is visible to query i iff j <= i (top-left alignment, also
+ *     when Sq != Sk).
+ *   - log-sum-exp: LSE_i = ln sum_j exp(scale * q_i . k_j) over visible keys, of
+ *     the scores before dropout; fp32, contiguous [B, H, Sq].
+ *   - dropout: inverted dropout applied to the normalised probabilities: a kept
+ *     element is scaled by 1/(1 - p).  The keep bit of element (b, h, i, j) is
+ *     Philox-4x32-10 (Salmon et al., SC'11) with key (low, high word of seed)
+ *     and counter (low, high word of offset + g, 0, 0), word j % 4, where
+ *     g = ((b*H + h)*Sq + i) * ceil(Sk/4) + j/4; kept iff the word is
+ *     >= floor(p * 2^32).  The index is absolute, so forward and backward
+ *     regenerate the same mask whatever their tiling (PyTorch PR "REDO of
+ *     dropout support for mem eff", Summary: RNG state handed from forward to
+ *     backward; absolute index for RNG state indexing).
+ *   - E == Ev is required (nvFuser issue 2278, the SdpaFwdOp follow-up).
+ *
+ * Tensors: logical shape [B, H, S, E] with arbitrary element strides for the
+ * first three dimensions and unit stride for E.  This covers both stride orders
+ * of the nvFuser test: BHSE (memory [b, h, s, e]) and BSHE (memory [b, s, h, e]).
+ * Supported now: dtype bf16, E in {64, 128}; data pointers 16-byte aligned and
+ * the first three strides multiples of 8 elements.
+ *
+ * Memory: every buffer is owned by the caller and lives on the current HIP
+ * device; the library never allocates or frees device memory.  All work is
+ * enqueued on `stream` and no call synchronises the device (except
+ * sdpa_profile_read).
+ *
+ * Errors: every compute call returns an sdpa_status.  On a validation error
+ * nothing is enqueued, outputs and the RNG state are untouched, and
+ * sdpa_last_error() (per thread) describes the problem.  No C++ exception
+ * crosses this boundary.
+ */
+#ifndef SDPA14_H
+#define SDPA14_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t; NULL means the default stream. */
+typedef struct ihipStream_t* sdpa_stream_t;
+
+typedef enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_INVALID = 1,     /* null pointer, shape mismatch, E != Ev, p not in [0,1), bad scale */
+  SDPA_ERR_UNSUPPORTED = 2, /* dtype, head dim, stride or alignment this build does not handle */
+  SDPA_ERR_WORKSPACE = 3,   /* backward workspace smaller than sdpa_bwd_workspace_size() */
+  SDPA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} sdpa_status;
+
+typedef enum sdpa_dtype { SDPA_BF16 = 0 } sdpa_dtype;
+
+/* A strided device tensor with logical shape [B, H, S, E]. */
+typedef struct sdpa_tensor {
+  void* data;        /* device pointer, 16-byte aligned */
+  int32_t dtype;     /* sdpa_dtype */
+  int64_t size[4];   /* B, H, S, E */
+  int64_t stride[4]; /* in elements; stride[3] must be 1 */
+} sdpa_tensor;
+
+/*
+ * Forward (sdpfa_fwd).
+ *   q [B,H,Sq,E], k [B,H,Sk,E], v [B,H,Sk,E]  inputs, bf16.
+ *   out [B,H,Sq,E]  output, bf16, any supported strides (usually q's).
+ *   lse             output, fp32, contiguous [B,H,Sq] (B*H*Sq floats).
+ *   seed, offset    host outputs: the Philox state this call used.  When
+ *                   dropout_p > 0 the library state's offset then advances by
+ *                   B*H*Sq*ceil(Sk/4); when dropout_p == 0 nothing advances
+ *                   and no random bits are used.
+ */
+int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+             double dropout_p, int is_causal, double scale,
+             const sdpa_tensor* out, float* lse,
+             uint64_t* seed, uint64_t* offset, sdpa_stream_t stream);
+
+/* Bytes of device workspace sdpa_bwd needs: D (fp32 [B,H,Sq]) and the fp32 dQ
+ * accumulator ([B,H,Sq,E]), each 256-byte aligned. */
+size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t E);
+
+/*
+ * Backward (sdpfa_bwd).
+ *   dout, q, k, v, out  bf16 inputs (out and lse as returned by sdpa_fwd).
+ *   seed, offset        the values sdpa_fwd returned; ignored when dropout_p == 0.
+ *   dq, dk, dv          bf16 outputs shaped like q, k, v (any supported strides).
+ *   workspace           device buffer of at least sdpa_bwd_workspace_size() bytes,
+ *                       256-byte aligned; its contents on entry do not matter.
+ * Three kernels run in order on `stream`: D = rowsum(dO * O) plus zeroing of the
+ * dQ accumulator, the key-block-parallel main pass (dK, dV, and dQ by fp32
+ * atomics), and the dQ conversion to bf16.
+ */
+int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+             const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
+             double dropout_p, int is_causal, uint64_t seed, uint64_t offset, double scale,
+             const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
+             void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
+
+/* Library-global Philox state (process wide, mutex guarded).  Default (0, 0). */
+void sdpa_set_rng_state(uint64_t seed, uint64_t offset);
+void sdpa_get_rng_state(uint64_t* seed, uint64_t* offset);
+
+/* Static name of a status code, and the calling thread's last error detail. */
+const char* sdpa_status_string(int status);
+const char* sdpa_last_error(void);
+
+/*
+ * Test hook: writes the dropout keep mask the kernels use, as bytes 0/1, to the
+ * device buffer mask [B*H*Sq*Sk] (contiguous b, h, i, j), for the given state
+ * and probability.  It uses the same device Philox code as the compute kernels.
+ */
+int sdpa_debug_dropout_mask(uint64_t seed, uint64_t offset, double dropout_p,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                            uint8_t* mask, sdpa_stream_t stream);
+
+/*
+ * Kernel timing by HIP events, for measurement.  While enabled, every kernel
+ * the library launches is bracketed by a pair of events on its own stream.
+ * sdpa_profile_read waits for the recorded events, returns the summed duration
+ * (ms) and launch count of one kernel kind since the last read, and clears
+ * that kind.  Kinds: 0 forward, 1 backward D/zeroing pass, 2 backward main
+ * pass, 3 dQ conversion.  At most 8192 launches are kept per kind; further
+ * launches are not timed.
+ */
+enum { SDPA_KERNEL_FWD = 0, SDPA_KERNEL_BWD_PRE = 1, SDPA_KERNEL_BWD_MAIN = 2,
+       SDPA_KERNEL_BWD_DQ = 3, SDPA_KERNEL_KINDS = 4 };
+int sdpa_profile_enable(int on);
+int sdpa_profile_read(int kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA14_H */

@@ -1,0 +1,30 @@
+"""Fused scaled-dot-product attention for AMD MI355X (gfx950).
+
+The compute lives in ``libsdpa14.so`` (hand-written HIP kernels behind the C ABI
+declared in ``include/sdpa14.h``); this package is its thin Python binding.
+
+    out, lse, seed, offset = sdpa_fwd(q, k, v, dropout_p, is_causal, scale)
+    dq, dk, dv = sdpa_bwd(dout, q, k, v, out, lse, dropout_p, is_causal, seed, offset, scale)
+
+Tensors are bf16, logical [B, H, S, E], BHSE or BSHE stride order, E in {64, 128}.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    KERNEL_BWD_DQ,
+    KERNEL_BWD_MAIN,
+    KERNEL_BWD_PRE,
+    KERNEL_FWD,
+    LIB_PATH,
+    SdpaError,
+    describe,
+    load_library,
+    sdpa_bwd,
+    sdpa_bwd_workspace_size,
+    sdpa_debug_dropout_mask,
+    sdpa_fwd,
+    sdpa_get_rng_state,
+    sdpa_profile_enable,
+    sdpa_profile_read,
+    sdpa_set_rng_state,
+)

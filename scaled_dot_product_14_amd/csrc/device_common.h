@@ -1,0 +1,94 @@
+// Device helpers for the gfx950 (CDNA4) attention kernels: bf16 MFMA tiles,
+// LDS transposed reads and cross-half wavefront exchange.
+//
+// Lane layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row l%32, k = 8*(l/32) + 0..7 (8 bf16)
+//     B: lane l holds col l%32, k = 8*(l/32) + 0..7 (8 bf16)
+//     C: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, col l%32
+//   ds_read_b64_tr_b16 (16-lane groups): lane j of a group receives element
+//     j%4 of the 4 x 16-bit words addressed by lanes 4*i + j/4, i = 0..3.  When
+//     lane j addresses row r0 + j/4, columns c0 + 4*(j%4) .. +3 of a row-major
+//     16-bit matrix, lane j receives column c0 + j, rows r0 .. r0+3: a
+//     transposed 4x16 read.
+//   permlane32_swap(x, x) gives {x[l], x[l+32]} on lanes < 32 and
+//     {x[l-32], x[l]} on lanes >= 32, so combining both halves of the result
+//     reduces over the lane pair (l, l^32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa14 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.f;
+  return z;
+}
+
+// 16-byte global load of 8 bf16.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// 16-byte LDS load of 8 bf16.
+__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposed 64-bit LDS read (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_tr4(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Maximum / sum over the lane pair (l, l^32).
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round four floats to bf16 (nearest even) and pack them into 8 bytes.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  v[2] = (__bf16)c;
+  v[3] = (__bf16)d;
+  return __builtin_bit_cast(uint2, v);
+}
+
+}  // namespace sdpa14

@@ -1,0 +1,67 @@
+// Kernel parameter blocks and launchers shared by the C ABI layer and the
+// kernel translation units.  Host-visible; no device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "philox.h"
+
+namespace sdpa14 {
+
+// Element strides of a logical [B, H, S, E] tensor (E has unit stride).
+struct Strides {
+  int64_t b, h, s;
+};
+
+struct FwdParams {
+  const uint16_t* q;  // bf16 bits
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // contiguous [B, H, Sq]
+  Strides sq, sk, sv, so;
+  int B, H, Sq, Sk;
+  float scale_log2;  // scale * log2(e)
+  DropoutParams drop;
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const float* lse;  // contiguous [B, H, Sq]
+  float* delta;      // workspace: D = rowsum(dO * O), contiguous [B, H, Sq]
+  float* dq_acc;     // workspace: fp32 dQ, contiguous [B, H, Sq, E]
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  int B, H, Sq, Sk;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  DropoutParams drop;
+};
+
+struct MaskParams {
+  uint8_t* mask;  // [B, H, Sq, Sk] bytes
+  int B, H, Sq, Sk;
+  DropoutParams drop;
+};
+
+// Tile choices the launchers take; 0 lets the launcher decide.
+struct TileChoice {
+  int fwd_waves;  // waves per forward workgroup (32 query rows each)
+};
+
+hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
+                      const TileChoice& tiles, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdParams& p, int E, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdParams& p, int E, bool causal, bool dropout,
+                           hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int E, hipStream_t stream);
+hipError_t launch_mask(const MaskParams& p, hipStream_t stream);
+
+}  // namespace sdpa14

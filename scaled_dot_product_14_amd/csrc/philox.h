@@ -1,0 +1,72 @@
+// Philox-4x32-10 on the device, and the dropout keep test built on it.
+//
+// Generator: Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+// 1, 2, 3" (SC'11).  Each round forms the two 32x32->64-bit products of
+// counter words 0 and 2 with fixed odd multipliers; the new counter is
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0).  The key words advance by two Weyl
+// constants between rounds.
+//
+// Use for dropout: the PyTorch PR "REDO of dropout support for mem eff"
+// (Summary) hands the RNG state from forward to backward and indexes the
+// stream by the absolute position of each score element.  Here one call
+// covers four consecutive keys j = 4c..4c+3 of query row i of head (b, h):
+// counter = offset + ((b*H + h)*Sq + i) * ceil(Sk/4) + c, key = seed, and key
+// j takes output word j % 4.  An element is kept iff its word is >= the
+// threshold floor(p * 2^32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa14 {
+
+struct PhiloxOut {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ PhiloxOut philox4x32_10(uint64_t counter, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+  uint32_t c0 = static_cast<uint32_t>(counter);
+  uint32_t c1 = static_cast<uint32_t>(counter >> 32);
+  uint32_t c2 = 0u, c3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint32_t hi0 = __umulhi(kM0, c0), lo0 = kM0 * c0;
+    const uint32_t hi1 = __umulhi(kM1, c2), lo1 = kM1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0;
+    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  PhiloxOut o;
+  o.w[0] = c0;
+  o.w[1] = c1;
+  o.w[2] = c2;
+  o.w[3] = c3;
+  return o;
+}
+
+// Dropout parameters shared by the kernels.
+struct DropoutParams {
+  uint64_t offset;     // Philox offset of this forward call
+  uint32_t seed_lo;    // key word 0
+  uint32_t seed_hi;    // key word 1
+  uint32_t threshold;  // floor(p * 2^32); keep iff word >= threshold
+  float keep_scale;    // 1 / (1 - p), rounded to fp32 on the host
+};
+
+// Counter of query row `row` of head `bh` for key group 0; key group c adds c.
+__device__ __forceinline__ uint64_t philox_row_base(const DropoutParams& d, int bh, int Sq,
+                                                    int row, int sk4) {
+  return d.offset + (static_cast<uint64_t>(bh) * static_cast<uint64_t>(Sq) +
+                     static_cast<uint64_t>(row)) * static_cast<uint64_t>(sk4);
+}
+
+}  // namespace sdpa14

@@ -1,0 +1,410 @@
+// C ABI of libsdpa14: argument validation, stride resolution, the Philox
+// state handed from forward to backward, workspace sizing, launches and
+// optional event timing.  The compute itself lives in fwd.hip / bwd.hip.
+//
+// The forward returns (out, lse, seed, offset) and the backward consumes
+// (seed, offset), as in the sdpfa_fwd / sdpfa_bwd pair of the nvFuser PR "DID
+// loop split for SDPA"; the RNG state travels from forward to backward instead
+// of a stored mask (PyTorch PR "REDO of dropout support for mem eff", Summary).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "kernels.h"
+#include "sdpa14.h"
+
+using namespace sdpa14;
+
+namespace {
+
+thread_local std::string t_last_error;
+
+std::mutex g_rng_mu;
+uint64_t g_rng_seed = 0;
+uint64_t g_rng_offset = 0;
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_last_error = buf;
+  return code;
+}
+
+struct Desc {
+  const uint16_t* ptr;
+  int64_t B, H, S, E;
+  Strides st;
+};
+
+// Validates one tensor descriptor and resolves its strides.  Strides of
+// size-1 dimensions never matter and are taken as 0.
+int check_tensor(const sdpa_tensor* t, const char* name, Desc* d) {
+  if (t == nullptr) return fail(SDPA_ERR_INVALID, "%s: descriptor is NULL", name);
+  if (t->data == nullptr) return fail(SDPA_ERR_INVALID, "%s: data pointer is NULL", name);
+  for (int i = 0; i < 4; ++i)
+    if (t->size[i] < 1)
+      return fail(SDPA_ERR_INVALID, "%s: size[%d] = %lld must be >= 1", name, i,
+                  (long long)t->size[i]);
+  if (t->dtype != SDPA_BF16)
+    return fail(SDPA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (bf16 only)", name, t->dtype);
+  if (t->stride[3] != 1 && t->size[3] > 1)
+    return fail(SDPA_ERR_UNSUPPORTED, "%s: stride of the head dim is %lld, must be 1", name,
+                (long long)t->stride[3]);
+  int64_t st[3];
+  for (int i = 0; i < 3; ++i) {
+    st[i] = (t->size[i] == 1) ? 0 : t->stride[i];
+    if (st[i] < 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "%s: negative stride[%d] is not supported", name, i);
+    if (st[i] % 8 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "%s: stride[%d] = %lld is not a multiple of 8 elements (16-byte rows)", name, i,
+                  (long long)st[i]);
+  }
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "%s: data pointer is not 16-byte aligned", name);
+  if (t->size[2] > kMaxSeq) return fail(SDPA_ERR_UNSUPPORTED, "%s: sequence too long", name);
+  if (t->size[0] * t->size[1] > kMaxGrid / 64)
+    return fail(SDPA_ERR_UNSUPPORTED, "%s: batch*heads too large", name);
+  d->ptr = static_cast<const uint16_t*>(t->data);
+  d->B = t->size[0];
+  d->H = t->size[1];
+  d->S = t->size[2];
+  d->E = t->size[3];
+  d->st = Strides{st[0], st[1], st[2]};
+  return SDPA_OK;
+}
+
+bool same_shape(const Desc& a, const Desc& b) {
+  return a.B == b.B && a.H == b.H && a.S == b.S && a.E == b.E;
+}
+
+int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
+  if (q.B != k.B || q.B != v.B || q.H != k.H || q.H != v.H)
+    return fail(SDPA_ERR_INVALID, "q, k, v disagree on batch or heads");
+  if (k.S != v.S) return fail(SDPA_ERR_INVALID, "k and v have different key lengths");
+  if (q.E != k.E) return fail(SDPA_ERR_INVALID, "q and k have different head dims");
+  if (v.E != q.E) return fail(SDPA_ERR_INVALID, "value head dim Ev = %lld differs from E = %lld",
+                              (long long)v.E, (long long)q.E);
+  if (q.E != 64 && q.E != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not supported (64 or 128)",
+                (long long)q.E);
+  const int64_t grid_f = q.B * q.H * ((q.S + 31) / 32);
+  if (grid_f > kMaxGrid) return fail(SDPA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return SDPA_OK;
+}
+
+int check_dropout(double p) {
+  if (!(p >= 0.0 && p < 1.0)) return fail(SDPA_ERR_INVALID, "dropout_p = %g not in [0, 1)", p);
+  return SDPA_OK;
+}
+
+int resolve_scale(double scale, int64_t E, float* out) {
+  if (isnan(scale)) {
+    *out = (float)(1.0 / sqrt((double)E));
+    return SDPA_OK;
+  }
+  if (!(isfinite(scale) && scale > 0.0))
+    return fail(SDPA_ERR_INVALID, "scale = %g must be finite and > 0 (NaN selects 1/sqrt(E))",
+                scale);
+  *out = (float)scale;
+  return SDPA_OK;
+}
+
+DropoutParams make_dropout(double p, uint64_t seed, uint64_t offset) {
+  DropoutParams d;
+  d.offset = offset;
+  d.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  d.seed_hi = (uint32_t)(seed >> 32);
+  d.threshold = (uint32_t)floor(p * 4294967296.0);
+  d.keep_scale = (float)(1.0 / (1.0 - p));
+  return d;
+}
+
+uint64_t offset_advance(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
+  return (uint64_t)B * (uint64_t)H * (uint64_t)Sq * (uint64_t)((Sk + 3) / 4);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- event timing -----------------------------------------------------------
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> used[SDPA_KERNEL_KINDS];
+};
+Profiler g_prof;
+constexpr size_t kMaxTimed = 8192;
+
+template <typename F>
+hipError_t timed_launch(int kind, hipStream_t stream, F launch) {
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.on && g_prof.used[kind].size() < kMaxTimed) {
+      if (!g_prof.pool.empty()) {
+        ev = g_prof.pool.back();
+        g_prof.pool.pop_back();
+      } else {
+        if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess)
+          ev = {nullptr, nullptr};
+      }
+    }
+  }
+  if (ev.first == nullptr) return launch();
+  (void)hipEventRecord(ev.first, stream);
+  const hipError_t err = launch();
+  (void)hipEventRecord(ev.second, stream);
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.used[kind].push_back(ev);
+  return err;
+}
+
+int hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return SDPA_OK;
+  return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+TileChoice tile_choice() {
+  static const TileChoice tc = [] {
+    TileChoice t{0};
+    if (const char* s = getenv("SDPA14_FWD_WAVES")) t.fwd_waves = atoi(s);
+    return t;
+  }();
+  return tc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+             double dropout_p, int is_causal, double scale, const sdpa_tensor* out, float* lse,
+             uint64_t* seed, uint64_t* offset, sdpa_stream_t stream) {
+  Desc dq, dk, dv, dout;
+  int rc;
+  if ((rc = check_tensor(q, "q", &dq))) return rc;
+  if ((rc = check_tensor(k, "k", &dk))) return rc;
+  if ((rc = check_tensor(v, "v", &dv))) return rc;
+  if ((rc = check_tensor(out, "out", &dout))) return rc;
+  if ((rc = check_qkv(dq, dk, dv))) return rc;
+  if (!same_shape(dq, dout)) return fail(SDPA_ERR_INVALID, "out must have q's shape");
+  if (lse == nullptr) return fail(SDPA_ERR_INVALID, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "lse is not 4-byte aligned");
+  if ((rc = check_dropout(dropout_p))) return rc;
+  float sc;
+  if ((rc = resolve_scale(scale, dq.E, &sc))) return rc;
+
+  uint64_t s0, o0;
+  {
+    std::lock_guard<std::mutex> lk(g_rng_mu);
+    s0 = g_rng_seed;
+    o0 = g_rng_offset;
+    if (dropout_p > 0.0) g_rng_offset += offset_advance(dq.B, dq.H, dq.S, dk.S);
+  }
+  if (seed) *seed = s0;
+  if (offset) *offset = o0;
+
+  FwdParams p;
+  p.q = dq.ptr;
+  p.k = dk.ptr;
+  p.v = dv.ptr;
+  p.o = const_cast<uint16_t*>(dout.ptr);
+  p.lse = lse;
+  p.sq = dq.st;
+  p.sk = dk.st;
+  p.sv = dv.st;
+  p.so = dout.st;
+  p.B = (int)dq.B;
+  p.H = (int)dq.H;
+  p.Sq = (int)dq.S;
+  p.Sk = (int)dk.S;
+  p.scale_log2 = sc * 1.44269504088896340736f;
+  p.drop = make_dropout(dropout_p, s0, o0);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const hipError_t err = timed_launch(SDPA_KERNEL_FWD, st, [&] {
+    return launch_fwd(p, (int)dq.E, is_causal != 0, dropout_p > 0.0, tile_choice(), st);
+  });
+  return hip_status(err, "forward launch");
+}
+
+size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t E) {
+  (void)Sk;
+  if (B < 1 || H < 1 || Sq < 1 || E < 1) return 0;
+  const size_t rows = (size_t)B * (size_t)H * (size_t)Sq;
+  return align256(rows * sizeof(float)) + align256(rows * (size_t)E * sizeof(float));
+}
+
+int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+             const sdpa_tensor* v, const sdpa_tensor* out, const float* lse, double dropout_p,
+             int is_causal, uint64_t seed, uint64_t offset, double scale, const sdpa_tensor* dq,
+             const sdpa_tensor* dk, const sdpa_tensor* dv, void* workspace,
+             size_t workspace_bytes, sdpa_stream_t stream) {
+  Desc ddo, dqi, dki, dvi, dout_i, dqo, dko, dvo;
+  int rc;
+  if ((rc = check_tensor(dout, "dout", &ddo))) return rc;
+  if ((rc = check_tensor(q, "q", &dqi))) return rc;
+  if ((rc = check_tensor(k, "k", &dki))) return rc;
+  if ((rc = check_tensor(v, "v", &dvi))) return rc;
+  if ((rc = check_tensor(out, "out", &dout_i))) return rc;
+  if ((rc = check_tensor(dq, "dq", &dqo))) return rc;
+  if ((rc = check_tensor(dk, "dk", &dko))) return rc;
+  if ((rc = check_tensor(dv, "dv", &dvo))) return rc;
+  if ((rc = check_qkv(dqi, dki, dvi))) return rc;
+  if (!same_shape(dqi, ddo)) return fail(SDPA_ERR_INVALID, "dout must have q's shape");
+  if (!same_shape(dqi, dout_i)) return fail(SDPA_ERR_INVALID, "out must have q's shape");
+  if (!same_shape(dqi, dqo)) return fail(SDPA_ERR_INVALID, "dq must have q's shape");
+  if (!same_shape(dki, dko)) return fail(SDPA_ERR_INVALID, "dk must have k's shape");
+  if (!same_shape(dvi, dvo)) return fail(SDPA_ERR_INVALID, "dv must have v's shape");
+  if (lse == nullptr) return fail(SDPA_ERR_INVALID, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "lse is not 4-byte aligned");
+  if ((rc = check_dropout(dropout_p))) return rc;
+  float sc;
+  if ((rc = resolve_scale(scale, dqi.E, &sc))) return rc;
+  const size_t need = sdpa_bwd_workspace_size(dqi.B, dqi.H, dqi.S, dki.S, dqi.E);
+  if (workspace == nullptr) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(SDPA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+
+  BwdParams p;
+  p.q = dqi.ptr;
+  p.k = dki.ptr;
+  p.v = dvi.ptr;
+  p.o = dout_i.ptr;
+  p.dout = ddo.ptr;
+  p.dq = const_cast<uint16_t*>(dqo.ptr);
+  p.dk = const_cast<uint16_t*>(dko.ptr);
+  p.dv = const_cast<uint16_t*>(dvo.ptr);
+  p.lse = lse;
+  const size_t rows = (size_t)dqi.B * dqi.H * dqi.S;
+  p.delta = static_cast<float*>(workspace);
+  p.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
+  p.sq = dqi.st;
+  p.sk = dki.st;
+  p.sv = dvi.st;
+  p.so = dout_i.st;
+  p.sdo = ddo.st;
+  p.sdq = dqo.st;
+  p.sdk = dko.st;
+  p.sdv = dvo.st;
+  p.B = (int)dqi.B;
+  p.H = (int)dqi.H;
+  p.Sq = (int)dqi.S;
+  p.Sk = (int)dki.S;
+  p.scale = sc;
+  p.scale_log2 = sc * 1.44269504088896340736f;
+  p.drop = make_dropout(dropout_p, seed, offset);
+  const int E = (int)dqi.E;
+  const bool causal = is_causal != 0, drop = dropout_p > 0.0;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t err = timed_launch(SDPA_KERNEL_BWD_PRE, st, [&] { return launch_bwd_pre(p, E, st); });
+  if (err != hipSuccess) return hip_status(err, "backward preprocess launch");
+  err = timed_launch(SDPA_KERNEL_BWD_MAIN, st,
+                     [&] { return launch_bwd_main(p, E, causal, drop, st); });
+  if (err != hipSuccess) return hip_status(err, "backward main launch");
+  err = timed_launch(SDPA_KERNEL_BWD_DQ, st, [&] { return launch_bwd_dq(p, E, st); });
+  return hip_status(err, "backward dQ launch");
+}
+
+void sdpa_set_rng_state(uint64_t seed, uint64_t offset) {
+  std::lock_guard<std::mutex> lk(g_rng_mu);
+  g_rng_seed = seed;
+  g_rng_offset = offset;
+}
+
+void sdpa_get_rng_state(uint64_t* seed, uint64_t* offset) {
+  std::lock_guard<std::mutex> lk(g_rng_mu);
+  if (seed) *seed = g_rng_seed;
+  if (offset) *offset = g_rng_offset;
+}
+
+const char* sdpa_status_string(int status) {
+  switch (status) {
+    case SDPA_OK: return "SDPA_OK";
+    case SDPA_ERR_INVALID: return "SDPA_ERR_INVALID";
+    case SDPA_ERR_UNSUPPORTED: return "SDPA_ERR_UNSUPPORTED";
+    case SDPA_ERR_WORKSPACE: return "SDPA_ERR_WORKSPACE";
+    case SDPA_ERR_HIP: return "SDPA_ERR_HIP";
+    default: return "SDPA_ERR_UNKNOWN";
+  }
+}
+
+const char* sdpa_last_error(void) { return t_last_error.c_str(); }
+
+int sdpa_debug_dropout_mask(uint64_t seed, uint64_t offset, double dropout_p, int64_t B,
+                            int64_t H, int64_t Sq, int64_t Sk, uint8_t* mask,
+                            sdpa_stream_t stream) {
+  if (mask == nullptr) return fail(SDPA_ERR_INVALID, "mask is NULL");
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return fail(SDPA_ERR_INVALID, "sizes must be >= 1");
+  if (Sq > kMaxSeq || Sk > kMaxSeq || B * H > kMaxGrid / 64)
+    return fail(SDPA_ERR_UNSUPPORTED, "problem too large");
+  if (B * H * Sq * ((Sk + 3) / 4) / 256 > kMaxGrid)
+    return fail(SDPA_ERR_UNSUPPORTED, "problem too large for one launch");
+  int rc;
+  if ((rc = check_dropout(dropout_p))) return rc;
+  MaskParams p;
+  p.mask = mask;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.Sq = (int)Sq;
+  p.Sk = (int)Sk;
+  p.drop = make_dropout(dropout_p, seed, offset);
+  (void)hipGetLastError();
+  return hip_status(launch_mask(p, reinterpret_cast<hipStream_t>(stream)), "mask launch");
+}
+
+int sdpa_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = on != 0;
+  return SDPA_OK;
+}
+
+int sdpa_profile_read(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= SDPA_KERNEL_KINDS) return fail(SDPA_ERR_INVALID, "bad kernel kind");
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    evs.swap(g_prof.used[kind]);
+  }
+  double sum = 0.0;
+  int64_t n = 0;
+  hipError_t first_err = hipSuccess;
+  for (auto& ev : evs) {
+    hipError_t err = hipEventSynchronize(ev.second);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, ev.first, ev.second);
+    if (err == hipSuccess) {
+      sum += ms;
+      ++n;
+    } else if (first_err == hipSuccess) {
+      first_err = err;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    for (auto& ev : evs) g_prof.pool.push_back(ev);
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = n;
+  return hip_status(first_err, "event timing");
+}
+
+}  // extern "C"
