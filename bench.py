@@ -9,13 +9,14 @@ Prints ONE JSON line:
                 when causal; backward 2.5x forward) over the timed step time
   fwd / bwd     the same for forward-only and backward-only timed loops, and
                 their fraction of the bf16 dense MFMA peak
-  kernels       average duration of each kernel, from HIP events recorded by the
-                library around its own launches on its stream
+  kernels       average duration of the forward and the backward kernel, from
+                HIP events recorded by the library around its own launches on its
+                stream
   roofline      the dominant kernel against its roofline
   cpu_baseline  the fp64 CPU oracle on the host cores (a reported baseline)
 
 Options: --steps K --warmup W --gpus N (N must be 1), --no-cpu-baseline,
---workload NAME, --copy-bytes N (time a plain device copy of N bytes instead,
+--workload NAME, --shape B,H,Sq,Sk,E,causal[,p], --copy-bytes N (time a plain device copy of N bytes instead,
 for calibrating hardware byte counters).
 """
 
@@ -42,6 +43,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--shape", default="",
+                    help="B,H,Sq,Sk,E,causal[,p] instead of a named workload (exploration)")
     return ap.parse_args()
 
 
@@ -128,14 +131,19 @@ def main():
     import scaled_dot_product_14_amd as sdpa
     import workloads
 
-    w = workloads.WORKLOADS[args.workload]
+    if args.shape:
+        f = args.shape.split(",")
+        B, H, Sq, Sk, E, causal = (int(x) for x in f[:6])
+        p = float(f[6]) if len(f) > 6 else 0.0
+        w = workloads.Workload(f"shape_{args.shape}", B, H, Sq, Sk, E, "BHSE", bool(causal), p,
+                               7, rng_seed=1234 if p > 0 else 0)
+    else:
+        w = workloads.WORKLOADS[args.workload]
     log(f"workload {w}")
     q, k, v, do = workloads.make_inputs(w, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(sdpa.sdpa_bwd_workspace_size(w.B, w.H, w.Sq, w.Sk, w.E), dtype=torch.uint8,
-                     device="cuda")
     sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset)
     state = {}
 
@@ -146,7 +154,7 @@ def main():
     def bwd():
         s, o = state["so"]
         sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq, dk=dk,
-                      dv=dv, workspace=ws)
+                      dv=dv)
 
     def step():
         fwd()
@@ -164,8 +172,7 @@ def main():
     log(f"fwd {ms_fwd * 1e3:.2f} us, bwd {ms_bwd * 1e3:.2f} us")
 
     # Per-kernel durations: events recorded by the library around each launch.
-    names = {sdpa.KERNEL_FWD: "fwd", sdpa.KERNEL_BWD_PRE: "bwd_pre",
-             sdpa.KERNEL_BWD_MAIN: "bwd_main", sdpa.KERNEL_BWD_DQ: "bwd_dq"}
+    names = {sdpa.KERNEL_FWD: "fwd", sdpa.KERNEL_BWD: "bwd"}
     for kind in names:
         sdpa.sdpa_profile_read(kind)
     sdpa.sdpa_profile_enable(True)
@@ -180,30 +187,17 @@ def main():
     log(f"kernel averages (us): { {k_: round(v_['avg_us'], 2) for k_, v_ in kern.items()} }")
 
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
-    rows = w.B * w.H * w.Sq
-    pre_bytes = rows * w.E * 2 * 2 + rows * 4 + rows * w.E * 4  # read dO, O; write D, zero dQ_acc
-    dq_bytes = rows * w.E * 4 + rows * w.E * 2
-    kern["fwd"].update(algorithmic_tflop=f_fwd / 1e12)
-    kern["bwd_main"].update(algorithmic_tflop=f_bwd / 1e12)
-    kern["bwd_pre"].update(algorithmic_bytes=pre_bytes)
-    kern["bwd_dq"].update(algorithmic_bytes=dq_bytes)
-    for name in ("fwd", "bwd_main"):
+    kern["fwd"]["algorithmic_tflop"] = f_fwd / 1e12
+    kern["bwd"]["algorithmic_tflop"] = f_bwd / 1e12
+    for name in ("fwd", "bwd"):
         kk = kern[name]
         kk["tflops"] = kk["algorithmic_tflop"] / (kk["avg_us"] * 1e-6)
         kk["frac_peak"] = kk["tflops"] / PEAK_BF16_TFLOPS
-    for name in ("bwd_pre", "bwd_dq"):
-        kk = kern[name]
-        kk["GBps"] = kk["algorithmic_bytes"] / (kk["avg_us"] * 1e-6) / 1e9
-        kk["frac_hbm"] = kk["GBps"] / PEAK_HBM_GBS
     dominant = max(kern, key=lambda n: kern[n]["avg_us"])
     dk_ = kern[dominant]
-    if "tflops" in dk_:
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
-                "traffic": None}
-    else:
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": dk_["GBps"], "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk_["frac_hbm"], "traffic": None}
+    roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
+            "traffic": None}
 
     result = {
         "metric": METRIC,

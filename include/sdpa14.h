@@ -63,7 +63,7 @@ typedef enum sdpa_status {
   SDPA_OK = 0,
   SDPA_ERR_INVALID = 1,     /* null pointer, shape mismatch, E != Ev, p not in [0,1), bad scale */
   SDPA_ERR_UNSUPPORTED = 2, /* dtype, head dim, stride or alignment this build does not handle */
-  SDPA_ERR_WORKSPACE = 3,   /* backward workspace smaller than sdpa_bwd_workspace_size() */
+  SDPA_ERR_WORKSPACE = 3,   /* reserved (no call takes a workspace) */
   SDPA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } sdpa_status;
 
@@ -92,26 +92,21 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
              const sdpa_tensor* out, float* lse,
              uint64_t* seed, uint64_t* offset, sdpa_stream_t stream);
 
-/* Bytes of device workspace sdpa_bwd needs: D (fp32 [B,H,Sq]) and the fp32 dQ
- * accumulator ([B,H,Sq,E]), each 256-byte aligned. */
-size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t E);
-
 /*
  * Backward (sdpfa_bwd).
  *   dout, q, k, v, out  bf16 inputs (out and lse as returned by sdpa_fwd).
  *   seed, offset        the values sdpa_fwd returned; ignored when dropout_p == 0.
- *   dq, dk, dv          bf16 outputs shaped like q, k, v (any supported strides).
- *   workspace           device buffer of at least sdpa_bwd_workspace_size() bytes,
- *                       256-byte aligned; its contents on entry do not matter.
- * Three kernels run in order on `stream`: D = rowsum(dO * O) plus zeroing of the
- * dQ accumulator, the key-block-parallel main pass (dK, dV, and dQ by fp32
- * atomics), and the dQ conversion to bf16.
+ *   dq, dk, dv          bf16 outputs shaped like q, k, v (any supported strides);
+ *                       they must not overlap the inputs.
+ * One kernel runs on `stream`.  It needs no workspace: D = rowsum(dO * O) is
+ * formed on the fly, dK/dV come from key-block workgroups and dQ from
+ * query-block workgroups (no atomics), so all three are bitwise reproducible.
  */
 int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
              const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
              double dropout_p, int is_causal, uint64_t seed, uint64_t offset, double scale,
              const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
-             void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
+             sdpa_stream_t stream);
 
 /* Library-global Philox state (process wide, mutex guarded).  Default (0, 0). */
 void sdpa_set_rng_state(uint64_t seed, uint64_t offset);
@@ -135,12 +130,10 @@ int sdpa_debug_dropout_mask(uint64_t seed, uint64_t offset, double dropout_p,
  * the library launches is bracketed by a pair of events on its own stream.
  * sdpa_profile_read waits for the recorded events, returns the summed duration
  * (ms) and launch count of one kernel kind since the last read, and clears
- * that kind.  Kinds: 0 forward, 1 backward D/zeroing pass, 2 backward main
- * pass, 3 dQ conversion.  At most 8192 launches are kept per kind; further
- * launches are not timed.
+ * that kind.  Kinds: 0 forward kernel, 1 backward kernel.  At most 8192
+ * launches are kept per kind; further launches are not timed.
  */
-enum { SDPA_KERNEL_FWD = 0, SDPA_KERNEL_BWD_PRE = 1, SDPA_KERNEL_BWD_MAIN = 2,
-       SDPA_KERNEL_BWD_DQ = 3, SDPA_KERNEL_KINDS = 4 };
+enum { SDPA_KERNEL_FWD = 0, SDPA_KERNEL_BWD = 1, SDPA_KERNEL_KINDS = 2 };
 int sdpa_profile_enable(int on);
 int sdpa_profile_read(int kind, double* total_ms, int64_t* launches);
 

@@ -11,16 +11,13 @@ Tensors are bf16, logical [B, H, S, E], BHSE or BSHE stride order, E in {64, 128
 
 from ._binding import (  # noqa: F401
     EXPORTED,
-    KERNEL_BWD_DQ,
-    KERNEL_BWD_MAIN,
-    KERNEL_BWD_PRE,
+    KERNEL_BWD,
     KERNEL_FWD,
     LIB_PATH,
     SdpaError,
     describe,
     load_library,
     sdpa_bwd,
-    sdpa_bwd_workspace_size,
     sdpa_debug_dropout_mask,
     sdpa_fwd,
     sdpa_get_rng_state,

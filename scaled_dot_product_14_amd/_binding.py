@@ -24,12 +24,10 @@ SDPA_ERR_HIP = 4
 SDPA_BF16 = 0
 
 KERNEL_FWD = 0
-KERNEL_BWD_PRE = 1
-KERNEL_BWD_MAIN = 2
-KERNEL_BWD_DQ = 3
+KERNEL_BWD = 1
 
 EXPORTED = (
-    "sdpa_fwd", "sdpa_bwd_workspace_size", "sdpa_bwd", "sdpa_set_rng_state",
+    "sdpa_fwd", "sdpa_bwd", "sdpa_set_rng_state",
     "sdpa_get_rng_state", "sdpa_status_string", "sdpa_last_error",
     "sdpa_debug_dropout_mask", "sdpa_profile_enable", "sdpa_profile_read",
 )
@@ -66,11 +64,9 @@ def load_library(path: str = LIB_PATH):
     lib.sdpa_fwd.argtypes = [P, P, P, ctypes.c_double, ctypes.c_int, ctypes.c_double, P,
                              ctypes.c_void_p, u64p, u64p, ctypes.c_void_p]
     lib.sdpa_fwd.restype = ctypes.c_int
-    lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int64] * 5
-    lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_bwd.argtypes = [P, P, P, P, P, ctypes.c_void_p, ctypes.c_double, ctypes.c_int,
                              ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, P, P, P,
-                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                             ctypes.c_void_p]
     lib.sdpa_bwd.restype = ctypes.c_int
     lib.sdpa_set_rng_state.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
     lib.sdpa_set_rng_state.restype = None
@@ -152,27 +148,19 @@ def sdpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dropout_p: float
     return out, lse, seed.value, offset.value
 
 
-def sdpa_bwd_workspace_size(B: int, H: int, Sq: int, Sk: int, E: int) -> int:
-    return int(load_library().sdpa_bwd_workspace_size(B, H, Sq, Sk, E))
-
-
 def sdpa_bwd(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int,
-             offset: int, scale=None, dq=None, dk=None, dv=None, workspace=None):
+             offset: int, scale=None, dq=None, dk=None, dv=None):
     """Backward: returns ``(dq, dk, dv)`` laid out like q, k, v."""
     lib = load_library()
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    B, H, Sq, E = q.shape
-    need = sdpa_bwd_workspace_size(B, H, Sq, k.shape[2], E)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                           float(dropout_p), int(bool(is_causal)), int(seed), int(offset),
                           _scale_arg(scale), *(ctypes.byref(d) for d in descs[5:]),
-                          workspace.data_ptr(), workspace.numel(), _stream(q.device))
+                          _stream(q.device))
     _check(rc)
     return dq, dk, dv
 

@@ -24,8 +24,13 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["sdpa14_api.hip", "fwd.hip", "bwd.hip", "mask.hip"]
 
 ARCH = "gfx950"
-# Packed fp32 VALU instructions are switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Device code: packed fp32 VALU instructions are switched off; MFMA accumulators
+# stay in ordinary VGPRs (no AGPR round trips in the loops); NaNs are not
+# honoured so row maxima map to v_max3 without operand canonicalisation
+# (infinities still are: masked scores are -inf).  Host code keeps IEEE NaN
+# semantics, which the argument checks rely on.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=true", "-Xarch_device", "-fno-honor-nans"]
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",

@@ -5,23 +5,32 @@
 // for SDPA"; dropout regenerates the forward's mask from (seed, offset) and the
 // absolute element index (PyTorch PR "REDO of dropout support for mem eff").
 //
-// Three kernels, in stream order:
-//   1. bwd_pre:  D_i = sum_e dO_ie * O_ie (fp32), and zero the fp32 dQ accumulator.
-//                Memory-bound: one read of dO and O, one write of dQ_acc.
-//   2. bwd_main: key-block parallel.  A workgroup owns 128 keys (32 per wave),
-//                keeps K and V fragments in registers and dK, dV accumulators in
-//                registers, and walks the query tiles (64 rows each) that can see
-//                its keys.  Per wave and 32-row query block:
-//                  S   = Q K_w^T           (A = Q rows from LDS, B = K_w in registers)
-//                  dPd = dO V_w^T          (A = dO rows from LDS, B = V_w in registers)
-//                  P   = exp2(S*scale*log2e - LSE*log2e); dropout mask M;
-//                  dS  = P * (dPd*M - D) * scale
-//                  dV^T += dO^T (P*M)       (A = dO read transposed from LDS,
-//                  dK^T += Q^T dS            B = P*M / dS straight from registers)
-//                dS goes to LDS; then each wave computes one 32x32 block of
-//                  dQ = dS K                (A = dS, B = K, both read transposed)
-//                and adds it to the fp32 accumulator with global float atomics.
-//   3. bwd_dq:   dQ = bf16(dQ_acc) in q's stride order.
+// One launch, two workgroup roles, no atomics and no workspace:
+//
+//   dK/dV role  a 32-key block.  Each of the 4 waves keeps the block's K and V
+//               fragments and its own dK^T, dV^T accumulators in registers and
+//               walks every 4th 32-row query tile that can see the block:
+//                 S   = Q K^T, dPd = dO V^T        (lane = key, registers = rows)
+//                 Ps  = scale * exp(S*scale - LSE) (masked; dropout kept/scaled)
+//                 dS' = Ps * (dP - D)              (= scale * dS)
+//                 dV^T += dO^T Pd,  dK^T += Q^T dS'
+//               Q and dO rows arrive in registers already in the A-operand
+//               layout of S and dPd; a copy goes to a wave-private LDS tile for
+//               the transposed reads of dO^T and Q^T (ds_read_b64_tr_b16).
+//               D_i = rowsum(dO * O) is formed from O rows on the fly.  The
+//               four partial dK, dV are summed through LDS at the end.
+//   dQ role     a 32-row query block.  Each wave keeps the block's Q and dO
+//               fragments, D and LSE in registers and walks every 4th 32-key
+//               tile:  S^T = K Q^T, dP^T = V dO^T (lane = row), dS'^T as above,
+//               dQ^T += K^T dS'^T with K^T read transposed from a wave-private
+//               LDS copy of the tile and dS'^T taken straight from registers.
+//               The four partial dQ are summed through LDS at the end.
+//
+// Both roles recompute S and dP, so the backward does 7 products of 2*E flops
+// per visible score element (5 are counted).  In exchange dQ needs neither
+// fp32 atomics nor a zeroed accumulator nor a conversion pass, every output is
+// bitwise reproducible, and a small causal problem gets twice as many
+// independent workgroups.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,339 +39,408 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O) and dQ_acc = 0.
+// Per-wave LDS footprint (bytes) of both roles, and of the final reduction.
 template <int E>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int TPR = E / 8;        // threads per row, 8 elements each
-  constexpr int RPB = 256 / TPR;    // rows per workgroup
-  const int tid = threadIdx.x;
-  const int c = tid % TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;  // over B*H*Sq
-  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  float acc = 0.f;
-  if (row < rows) {
-    const int bh = (int)(row / p.Sq);
-    const int qi = (int)(row - (int64_t)bh * p.Sq);
-    const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-    const bf16x8 d = load_bf16x8(p.dout + b * p.sdo.b + h * p.sdo.h + (int64_t)qi * p.sdo.s + c * 8);
-    const bf16x8 o = load_bf16x8(p.o + b * p.so.b + h * p.so.h + (int64_t)qi * p.so.s + c * 8);
+struct BwdLds {
+  static constexpr int TP = E + 32;  // tile pitch (elements): conflict-free transposed reads
+  static constexpr int TILE = 32 * TP * 2;
+  static constexpr int WAVE = 2 * TILE + 64 * 4;   // dK/dV role: Q, dO tiles, D and LSE rows
+  static constexpr int RED = 4 * (E / 32) * 16 * 64 * 4;  // one fp32 accumulator per wave
+  static constexpr int TOTAL = (4 * WAVE > RED) ? 4 * WAVE : RED;
+};
+
+// Sums the four waves' accumulators acc[E/32] (C layout: lane = output row
+// row0 + l32, register r = column 32*eb + 8*(r/4) + 4*g + r%4), scales by mul and
+// stores bf16 rows below `limit`.  Wave w stores every 4th group of 4 columns.
+template <int E>
+__device__ __forceinline__ void reduce_store(const f32x16 (&acc)[E / 32], float mul,
+                                             uint16_t* dst, int64_t stride, int row0, int limit,
+                                             unsigned char* lds, int wave, int lane) {
+  constexpr int NEB = E / 32;
+  float* red = reinterpret_cast<float*>(lds);
+  __syncthreads();  // every wave is done with the LDS it used before
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf((float)d[i], (float)o[i], acc);
-    float4* z = reinterpret_cast<float4*>(p.dq_acc + row * E + c * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave * NEB + eb) * 16 + r) * 64 + lane] = acc[eb][r];
+  __syncthreads();
+  const int row = row0 + (lane & 31);
+  const int g = lane >> 5;
+#pragma unroll
+  for (int gi = wave; gi < NEB * 4; gi += 4) {
+    const int eb = gi >> 2, cg = gi & 3;
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) s += red[((w * NEB + eb) * 16 + 4 * cg + t) * 64 + lane];
+      v[t] = s * mul;
+    }
+    if (row < limit)
+      *reinterpret_cast<uint2*>(dst + (int64_t)row * stride + eb * 32 + 8 * cg + 4 * g) =
+          pack_bf16x4(v[0], v[1], v[2], v[3]);
   }
-#pragma unroll
-  for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m);
-  if (row < rows && c == 0) p.delta[row] = acc;
+}
+
+// Dropout keep bits for the dK/dV role.  The lane holds key `key` (key % 4 ==
+// lane % 4) and, for register group c, the four rows row0 + u, u = 0..3.  Lane t
+// of each quad evaluates the Philox call of row row0 + t for the key group of
+// the quad (four words: keys 4*(key/4) + 0..3), packs the four keep bits, and
+// every lane collects its own key's bit from the four lanes of its quad.
+// Returns bit u = keep(row0 + u, key).
+__device__ __forceinline__ uint32_t keep_bits_for_key(const DropoutParams& d, int bh, int Sq,
+                                                      int sk4, int row0, int key, int lane) {
+  const int t = lane & 3;
+  const uint64_t ctr = philox_row_base(d, bh, Sq, row0 + t, sk4) + (uint32_t)(key >> 2);
+  const PhiloxOut w = philox4x32_10(ctr, d.seed_lo, d.seed_hi);
+  const int nib = (w.w[0] >= d.threshold ? 1 : 0) | (w.w[1] >= d.threshold ? 2 : 0) |
+                  (w.w[2] >= d.threshold ? 4 : 0) | (w.w[3] >= d.threshold ? 8 : 0);
+  const int n0 = __builtin_amdgcn_mov_dpp(nib, 0x00, 0xF, 0xF, false);  // quad lane 0
+  const int n1 = __builtin_amdgcn_mov_dpp(nib, 0x55, 0xF, 0xF, false);  // quad lane 1
+  const int n2 = __builtin_amdgcn_mov_dpp(nib, 0xAA, 0xF, 0xF, false);  // quad lane 2
+  const int n3 = __builtin_amdgcn_mov_dpp(nib, 0xFF, 0xF, 0xF, false);  // quad lane 3
+  return ((n0 >> t) & 1) | (((n1 >> t) & 1) << 1) | (((n2 >> t) & 1) << 2) |
+         (((n3 >> t) & 1) << 3);
 }
 
 // ---------------------------------------------------------------------------
-// 2. Main pass.
 template <int E, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p, int n_kblocks) {
-  constexpr int BK = 128;     // keys per workgroup, 32 per wave
-  constexpr int BQ = 64;      // query rows per iteration
-  constexpr int QP = E + 8;   // Q / dO tile pitch (elements)
-  constexpr int KP = E + 8;   // K tile pitch
-  constexpr int SP = BQ + 8;  // dS tile pitch, stored [key][query]
-  constexpr int CPR = E / 8;  // 16-byte chunks per row
-  constexpr int QCH = BQ * CPR;
-  constexpr int QPER = (QCH + 255) / 256;
-  constexpr int NEB = E / 32;                    // 32-wide column blocks of E
-  constexpr int DQ_BLOCKS_PER_WAVE = (2 * NEB) / 4;  // dQ tile: 2 row blocks x NEB col blocks
-
-  __shared__ __attribute__((aligned(16))) uint16_t qs[BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t dos[BQ * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t kls[BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t dsl[BK * SP];
-  __shared__ float lse_s[BQ];
-  __shared__ float d_s[BQ];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  const int bh_count = p.B * p.H;
-  const int kblk = blockIdx.x / bh_count;  // key block 0 (most work when causal) first
-  const int bh = blockIdx.x - kblk * bh_count;
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  const int kb0 = kblk * BK;
-  const int kw0 = kb0 + 32 * wave;
-  const int key = kw0 + l32;  // key column of this lane in S / dP
+__device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
+                                          unsigned char* lds) {
+  constexpr int NES = E / 16, NEB = E / 32;
+  using L = BwdLds<E>;
+  constexpr int TP = L::TP;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int kb0 = kblk * 32;
+  const int key = kb0 + l32;
+  const float c = p.scale_log2;
+  const float lsc = __log2f(p.scale);
 
   const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
+  const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
+  const uint16_t* op = p.o + b * p.so.b + h * p.so.h;
   const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
   const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
-  const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
   const float* lsep = p.lse + (int64_t)bh * p.Sq;
-  const float* dlp = p.delta + (int64_t)bh * p.Sq;
-  float* dqa = p.dq_acc + (int64_t)bh * p.Sq * E;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp, (uint32_t)(((int64_t)(p.Sq - 1) * p.sq.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t dor = make_rsrc(dop, (uint32_t)(((int64_t)(p.Sq - 1) * p.sdo.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc(op, (uint32_t)(((int64_t)(p.Sq - 1) * p.so.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, (uint32_t)(((int64_t)(p.Sk - 1) * p.sk.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, (uint32_t)(((int64_t)(p.Sk - 1) * p.sv.s + E) * 2));
 
-  // K_w, V_w as B operands of S = Q K^T and dPd = dO V^T: lane = key, e = 16*es + 8*g + 0..7.
-  bf16x8 kf[E / 16], vf[E / 16];
+  // K, V of the block as B operands of S = Q K^T and dPd = dO V^T: lane = key,
+  // e = 16*es + 8*g + 0..7.  Keys past Sk read as zeros.
+  bf16x8 kf[NES], vf[NES];
 #pragma unroll
-  for (int es = 0; es < E / 16; ++es) {
-    if (key < p.Sk) {
-      kf[es] = load_bf16x8(kp + (int64_t)key * p.sk.s + es * 16 + 8 * g);
-      vf[es] = load_bf16x8(vp + (int64_t)key * p.sv.s + es * 16 + 8 * g);
-    } else {
-      kf[es] = zero_bf16x8();
-      vf[es] = zero_bf16x8();
-    }
-  }
-  // The whole K block in LDS (row-major) for the dQ product.
-  for (int cidx = tid; cidx < BK * CPR; cidx += 256) {
-    const int row = cidx / CPR, col = cidx - (cidx / CPR) * CPR;
-    const int kr = kb0 + row;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (kr < p.Sk) val = *reinterpret_cast<const uint4*>(kp + (int64_t)kr * p.sk.s + col * 8);
-    *reinterpret_cast<uint4*>(kls + row * KP + col * 8) = val;
+  for (int es = 0; es < NES; ++es) {
+    const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
+    kf[es] = __builtin_bit_cast(bf16x8, buffer_load16(kr, (uint32_t)key * (uint32_t)(p.sk.s * 2) + off16));
+    vf[es] = __builtin_bit_cast(bf16x8, buffer_load16(vr, (uint32_t)key * (uint32_t)(p.sv.s * 2) + off16));
   }
 
-  f32x16 dv_acc[NEB], dk_acc[NEB];
+  f32x16 dva[NEB], dka[NEB];
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
-    dv_acc[eb] = zero16();
-    dk_acc[eb] = zero16();
+    dva[eb] = zero16();
+    dka[eb] = zero16();
   }
 
-  const int n_qt = (p.Sq + BQ - 1) / BQ;
-  int qt_begin = 0;
-  if (CAUSAL) qt_begin = (kb0 < p.Sq) ? kb0 / BQ : n_qt;  // queries below kb0 see none of these keys
-
-  // Transposed-read addressing (device_common.h).  "perm": contraction slot
-  // (g, i) <-> row 8*(i/4) + 4*g + i%4, matching the C-register order of S.
-  // "nat": slot (g, i) <-> row 8*g + i.
-  const int tr_row_perm = 4 * g + ((lane & 15) >> 2);
-  const int tr_row_nat = 8 * g + ((lane & 15) >> 2);
+  const int nqt = (p.Sq + 31) / 32;
+  const int t0 = CAUSAL ? ((kb0 < p.Sq) ? kb0 / 32 : nqt) : 0;
+  uint16_t* ql = reinterpret_cast<uint16_t*>(lds + wave * L::WAVE);
+  uint16_t* dol = ql + 32 * TP;
+  float* rv = reinterpret_cast<float*>(dol + 32 * TP);  // D[32], LSE2[32]
+  // Transposed-read addressing: contraction slot (g, i) <-> tile row
+  // 8*(i/4) + 4*g + i%4 (the C-register order of S); see device_common.h.
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  const float c = p.scale_log2;
+  const uint32_t qs2 = (uint32_t)(p.sq.s * 2), dos2 = (uint32_t)(p.sdo.s * 2),
+                 os2 = (uint32_t)(p.so.s * 2);
   const int sk4 = (p.Sk + 3) >> 2;
 
-  uint4 qreg[QPER], doreg[QPER];
-  float lse_r = 0.f, d_r = 0.f;
-  auto load_tile = [&](int q0) {
+  bf16x8 qa[NES], doa[NES], oa[NES];
+  float lse_v = 0.f;
+  auto load_tile = [&](int t, bf16x8 (&q_)[NES], bf16x8 (&d_)[NES], bf16x8 (&o_)[NES], float& l_) {
+    const uint32_t row = (uint32_t)(t * 32 + l32);
 #pragma unroll
-    for (int i = 0; i < QPER; ++i) {
-      const int cidx = tid + i * 256;
-      const int row = cidx / CPR, col = cidx - (cidx / CPR) * CPR;
-      const int qr = q0 + row;
-      if (cidx < QCH && qr < p.Sq) {
-        qreg[i] = *reinterpret_cast<const uint4*>(qp + (int64_t)qr * p.sq.s + col * 8);
-        doreg[i] = *reinterpret_cast<const uint4*>(dop + (int64_t)qr * p.sdo.s + col * 8);
-      } else {
-        qreg[i] = make_uint4(0, 0, 0, 0);
-        doreg[i] = make_uint4(0, 0, 0, 0);
-      }
+    for (int es = 0; es < NES; ++es) {
+      const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
+      q_[es] = __builtin_bit_cast(bf16x8, buffer_load16(qr, row * qs2 + off16));
+      d_[es] = __builtin_bit_cast(bf16x8, buffer_load16(dor, row * dos2 + off16));
+      o_[es] = __builtin_bit_cast(bf16x8, buffer_load16(orr, row * os2 + off16));
     }
-    if (tid < BQ) {
-      const int qr = q0 + tid;
-      lse_r = (qr < p.Sq) ? lsep[qr] * kLog2e : 0.f;
-      d_r = (qr < p.Sq) ? dlp[qr] : 0.f;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < QPER; ++i) {
-      const int cidx = tid + i * 256;
-      if (cidx < QCH) {
-        const int row = cidx / CPR, col = cidx - (cidx / CPR) * CPR;
-        *reinterpret_cast<uint4*>(qs + row * QP + col * 8) = qreg[i];
-        *reinterpret_cast<uint4*>(dos + row * QP + col * 8) = doreg[i];
-      }
-    }
-    if (tid < BQ) {
-      lse_s[tid] = lse_r;
-      d_s[tid] = d_r;
-    }
+    l_ = ((int)row < p.Sq) ? lsep[row] : 0.f;
   };
 
-  if (qt_begin < n_qt) load_tile(qt_begin * BQ);
-  for (int qt = qt_begin; qt < n_qt; ++qt) {
-    const int q0 = qt * BQ;
-    __syncthreads();  // previous iteration is done with qs, dos, dsl
-    store_tile();
-    __syncthreads();
-    if (qt + 1 < n_qt) load_tile(q0 + BQ);
+  int t = t0 + wave;
+  if (t < nqt) load_tile(t, qa, doa, oa, lse_v);
+  for (; t < nqt; t += 4) {
+    const int q0 = t * 32;
+    // Stage the rows for the transposed reads, and the per-row D and LSE.
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      *reinterpret_cast<bf16x8*>(ql + l32 * TP + es * 16 + 8 * g) = qa[es];
+      *reinterpret_cast<bf16x8*>(dol + l32 * TP + es * 16 + 8 * g) = doa[es];
+    }
+    float dpart = 0.f;
+#pragma unroll
+    for (int es = 0; es < NES; ++es)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dpart = fmaf((float)doa[es][i], (float)oa[es][i], dpart);
+    const float dsum = pair_sum(dpart);
+    if (g == 0) {
+      rv[l32] = dsum;
+      rv[32 + l32] = lse_v * kLog2e - lsc;  // exp2(S*c - this) = scale * P
+    }
 
+    f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      const int qb = q0 + qh * 32;  // first query row of this 32-row block
-      uint16_t* dsw = dsl + (32 * wave + l32) * SP + qh * 32 + 4 * g;
-      if (CAUSAL && kw0 > qb + 31) {  // every key of this wave is after every row
+    for (int es = 0; es < NES; ++es) {
+      sacc = mfma32x32x16(qa[es], kf[es], sacc);
+      dpacc = mfma32x32x16(doa[es], vf[es], dpacc);
+    }
+    bf16x8 qn[NES], don[NES], on[NES];
+    float lsen = 0.f;
+    if (t + 4 < nqt) load_tile(t + 4, qn, don, on, lsen);
+    __builtin_amdgcn_wave_barrier();
+
+    // C layout: lane = key, register r = row q0 + 8*(r/4) + 4*g + r%4.
+    const bool need_mask = (CAUSAL && q0 == kb0) || (q0 + 31 >= p.Sq) || (kb0 + 31 >= p.Sk);
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
-        for (int cg = 0; cg < 4; ++cg) *reinterpret_cast<uint2*>(dsw + 8 * cg) = make_uint2(0, 0);
-        continue;
-      }
-      f32x16 sacc = zero16(), dpacc = zero16();
+    for (int cg = 0; cg < 4; ++cg) {
+      const float4 dv4 = *reinterpret_cast<const float4*>(rv + 8 * cg + 4 * g);
+      const float4 lv4 = *reinterpret_cast<const float4*>(rv + 32 + 8 * cg + 4 * g);
+      const float dvals[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+      const float lvals[4] = {lv4.x, lv4.y, lv4.z, lv4.w};
+      uint32_t kbits = 0xF;
+      if (DROPOUT) kbits = keep_bits_for_key(p.drop, bh, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
 #pragma unroll
-      for (int es = 0; es < E / 16; ++es) {
-        const bf16x8 aq = lds_bf16x8(qs + (qh * 32 + l32) * QP + es * 16 + 8 * g);
-        sacc = mfma32x32x16(aq, kf[es], sacc);
-        const bf16x8 ad = lds_bf16x8(dos + (qh * 32 + l32) * QP + es * 16 + 8 * g);
-        dpacc = mfma32x32x16(ad, vf[es], dpacc);
-      }
-      // C layout: lane = key, register r = query row qh*32 + 8*(r/4) + 4*g + r%4.
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = qh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const int qa = q0 + ql;
-        const bool ok = (qa < p.Sq) && (key < p.Sk) && (!CAUSAL || key <= qa);
-        const float pv = ok ? fast_exp2(fmaf(sacc[r], c, -lse_s[ql])) : 0.f;
-        float dp = dpacc[r];
-        float pd = pv;
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * cg + u;
+        const int qrow = q0 + 8 * cg + 4 * g + u;
+        bool ok = true;
+        if (need_mask) ok = (qrow < p.Sq) && (key < p.Sk) && (!CAUSAL || key <= qrow);
+        const float ps = ok ? fast_exp2(fmaf(sacc[r], c, -lvals[u])) : 0.f;
+        float dp = dpacc[r], pd = ps;
         if (DROPOUT) {
-          const uint64_t ctr = philox_row_base(p.drop, bh, p.Sq, qa, sk4) + (uint32_t)(key >> 2);
-          const PhiloxOut w = philox4x32_10(ctr, p.drop.seed_lo, p.drop.seed_hi);
-          const uint32_t word = w.w[key & 3];
-          const bool keep = word >= p.drop.threshold;
-          pd = keep ? pv * p.drop.keep_scale : 0.f;
+          const bool keep = (kbits >> u) & 1;
+          pd = keep ? ps * p.drop.keep_scale : 0.f;
           dp = keep ? dp * p.drop.keep_scale : 0.f;
         }
-        const float ds = pv * (dp - d_s[ql]) * p.scale;
         pb[r >> 3][r & 7] = (__bf16)pd;
-        dsb[r >> 3][r & 7] = (__bf16)ds;
-      }
-#pragma unroll
-      for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int rb = qh * 32 + 16 * hf + tr_row_perm;
-          const uint16_t* ad = dos + rb * QP + eb * 32 + tr_col;
-          dv_acc[eb] = mfma32x32x16(concat(lds_tr4(ad), lds_tr4(ad + 8 * QP)), pb[hf], dv_acc[eb]);
-          const uint16_t* aq = qs + rb * QP + eb * 32 + tr_col;
-          dk_acc[eb] = mfma32x32x16(concat(lds_tr4(aq), lds_tr4(aq + 8 * QP)), dsb[hf], dk_acc[eb]);
-        }
-      // dS to LDS as [key][query]: registers 4*cg..4*cg+3 are rows 8*cg + 4*g + 0..3.
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        bf16x4 v4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) v4[t] = dsb[(4 * cg + t) >> 3][(4 * cg + t) & 7];
-        *reinterpret_cast<uint2*>(dsw + 8 * cg) = __builtin_bit_cast(uint2, v4);
+        dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dvals[u]));
       }
     }
-    __syncthreads();  // dS of all four waves is in LDS
-
-    // dQ tile [64 rows x E] = dS [64 x 128] K [128 x E]; block (row half, column block).
-#pragma unroll
-    for (int bi = 0; bi < DQ_BLOCKS_PER_WAVE; ++bi) {
-      const int blk = wave * DQ_BLOCKS_PER_WAVE + bi;
-      const int rh = blk / NEB;   // 32-row half of the query tile
-      const int eb = blk % NEB;   // 32-wide column block
-      const int qmax = q0 + rh * 32 + 31;
-      if (CAUSAL && kb0 > qmax) continue;  // all of dS is zero here
-      int ks_end = BK / 16;
-      if (CAUSAL) ks_end = min(ks_end, (qmax - kb0) / 16 + 1);
-      f32x16 acc = zero16();
-      for (int ksx = 0; ksx < ks_end; ++ksx) {
-        const uint16_t* as = dsl + (ksx * 16 + tr_row_nat) * SP + rh * 32 + tr_col;
-        const uint16_t* bs = kls + (ksx * 16 + tr_row_nat) * KP + eb * 32 + tr_col;
-        const bf16x8 a = concat(lds_tr4(as), lds_tr4(as + 4 * SP));
-        const bf16x8 bb = concat(lds_tr4(bs), lds_tr4(bs + 4 * KP));
-        acc = mfma32x32x16(a, bb, acc);
-      }
-      // C layout: lane = column eb*32 + l32, register r = row rh*32 + 8*(r/4) + 4*g + r%4.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qa = q0 + rh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (qa < p.Sq) unsafeAtomicAdd(dqa + (int64_t)qa * E + eb * 32 + l32, acc[r]);
-      }
-    }
-  }
-
-  // dK^T, dV^T: lane = key, register r = column eb*32 + 8*(r/4) + 4*g + r%4.
-  if (key < p.Sk) {
-    uint16_t* dkp = p.dk + b * p.sdk.b + h * p.sdk.h + (int64_t)key * p.sdk.s;
-    uint16_t* dvp = p.dv + b * p.sdv.b + h * p.sdv.h + (int64_t)key * p.sdv.s;
 #pragma unroll
     for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        const int e = eb * 32 + 8 * cg + 4 * g;
-        *reinterpret_cast<uint2*>(dkp + e) =
-            pack_bf16x4(dk_acc[eb][4 * cg], dk_acc[eb][4 * cg + 1], dk_acc[eb][4 * cg + 2],
-                        dk_acc[eb][4 * cg + 3]);
-        *reinterpret_cast<uint2*>(dvp + e) =
-            pack_bf16x4(dv_acc[eb][4 * cg], dv_acc[eb][4 * cg + 1], dv_acc[eb][4 * cg + 2],
-                        dv_acc[eb][4 * cg + 3]);
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint16_t* ad = dol + (16 * hf + tr_row) * TP + eb * 32 + tr_col;
+        dva[eb] = mfma32x32x16(concat(lds_tr4(ad), lds_tr4(ad + 8 * TP)), pb[hf], dva[eb]);
+        const uint16_t* aq = ql + (16 * hf + tr_row) * TP + eb * 32 + tr_col;
+        dka[eb] = mfma32x32x16(concat(lds_tr4(aq), lds_tr4(aq + 8 * TP)), dsb[hf], dka[eb]);
       }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      qa[es] = qn[es];
+      doa[es] = don[es];
+      oa[es] = on[es];
+    }
+    lse_v = lsen;
   }
+
+  // dV = (1/scale) * sum(Pd^T dO) since Pd carries the scale; dK carries it already.
+  uint16_t* dvp = p.dv + b * p.sdv.b + h * p.sdv.h;
+  uint16_t* dkp = p.dk + b * p.sdk.b + h * p.sdk.h;
+  reduce_store<E>(dva, 1.f / p.scale, dvp, p.sdv.s, kb0, p.Sk, lds, wave, lane);
+  reduce_store<E>(dka, 1.f, dkp, p.sdk.s, kb0, p.Sk, lds, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = bf16(dQ_acc) in q's layout.
-template <int E>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-  constexpr int TPR = E / 8;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  const int64_t row = t / TPR;
-  if (row >= rows) return;
-  const int c = (int)(t - row * TPR);
-  const int bh = (int)(row / p.Sq);
-  const int qi = (int)(row - (int64_t)bh * p.Sq);
+template <int E, bool CAUSAL, bool DROPOUT>
+__device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
+  constexpr int NES = E / 16, NEB = E / 32;
+  using L = BwdLds<E>;
+  constexpr int TP = L::TP;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const float4* src = reinterpret_cast<const float4*>(p.dq_acc + row * E + c * 8);
-  const float4 x = src[0], y = src[1];
-  uint2 lo = pack_bf16x4(x.x, x.y, x.z, x.w);
-  uint2 hi = pack_bf16x4(y.x, y.y, y.z, y.w);
-  *reinterpret_cast<uint4*>(p.dq + b * p.sdq.b + h * p.sdq.h + (int64_t)qi * p.sdq.s + c * 8) =
-      make_uint4(lo.x, lo.y, hi.x, hi.y);
+  const int q0 = qblk * 32;
+  const int qrow = q0 + l32;
+  const float c = p.scale_log2;
+
+  const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
+  const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
+  const uint16_t* op = p.o + b * p.so.b + h * p.so.h;
+  const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
+  const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(qp, (uint32_t)(((int64_t)(p.Sq - 1) * p.sq.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t dor = make_rsrc(dop, (uint32_t)(((int64_t)(p.Sq - 1) * p.sdo.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t orr = make_rsrc(op, (uint32_t)(((int64_t)(p.Sq - 1) * p.so.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, (uint32_t)(((int64_t)(p.Sk - 1) * p.sk.s + E) * 2));
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, (uint32_t)(((int64_t)(p.Sk - 1) * p.sv.s + E) * 2));
+
+  // Q, dO of this row as B operands of S^T = K Q^T and dP^T = V dO^T; D and LSE of the row.
+  bf16x8 qf[NES], dof[NES];
+  float dpart = 0.f;
+#pragma unroll
+  for (int es = 0; es < NES; ++es) {
+    const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
+    qf[es] = __builtin_bit_cast(bf16x8, buffer_load16(qr, (uint32_t)qrow * (uint32_t)(p.sq.s * 2) + off16));
+    dof[es] = __builtin_bit_cast(bf16x8, buffer_load16(dor, (uint32_t)qrow * (uint32_t)(p.sdo.s * 2) + off16));
+    const bf16x8 o8 = __builtin_bit_cast(bf16x8, buffer_load16(orr, (uint32_t)qrow * (uint32_t)(p.so.s * 2) + off16));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dpart = fmaf((float)dof[es][i], (float)o8[i], dpart);
+  }
+  const float dsum = pair_sum(dpart);
+  const float lse2 =
+      ((qrow < p.Sq) ? p.lse[(int64_t)bh * p.Sq + qrow] * kLog2e : 0.f) - __log2f(p.scale);
+
+  f32x16 dqa[NEB];
+#pragma unroll
+  for (int eb = 0; eb < NEB; ++eb) dqa[eb] = zero16();
+
+  const int nkt = (p.Sk + 31) / 32;
+  const int kt_end = CAUSAL ? min(nkt, min(q0 + 31, p.Sq - 1) / 32 + 1) : nkt;
+  uint16_t* kl = reinterpret_cast<uint16_t*>(lds + wave * L::WAVE);
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint32_t ks2 = (uint32_t)(p.sk.s * 2), vs2 = (uint32_t)(p.sv.s * 2);
+  const int key_limit = CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1;
+  const int sk4 = (p.Sk + 3) >> 2;
+  uint64_t drow = 0;
+  if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
+
+  bf16x8 ka[NES], va[NES];
+  auto load_tile = [&](int j, bf16x8 (&k_)[NES], bf16x8 (&v_)[NES]) {
+    const uint32_t row = (uint32_t)(j * 32 + l32);
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
+      k_[es] = __builtin_bit_cast(bf16x8, buffer_load16(kr, row * ks2 + off16));
+      v_[es] = __builtin_bit_cast(bf16x8, buffer_load16(vr, row * vs2 + off16));
+    }
+  };
+
+  int j = wave;
+  if (j < kt_end) load_tile(j, ka, va);
+  for (; j < kt_end; j += 4) {
+    const int k0 = j * 32;
+#pragma unroll
+    for (int es = 0; es < NES; ++es)
+      *reinterpret_cast<bf16x8*>(kl + l32 * TP + es * 16 + 8 * g) = ka[es];
+
+    // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
+    f32x16 sacc = zero16(), dpacc = zero16();
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      sacc = mfma32x32x16(ka[es], qf[es], sacc);
+      dpacc = mfma32x32x16(va[es], dof[es], dpacc);
+    }
+    bf16x8 kn[NES], vn[NES];
+    if (j + 4 < kt_end) load_tile(j + 4, kn, vn);
+    __builtin_amdgcn_wave_barrier();
+
+    const bool need_mask = (k0 + 31 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1));
+    const int lim = key_limit - k0 - 4 * g;
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      uint32_t kbits = 0xF;
+      if (DROPOUT) {
+        const PhiloxOut w = philox4x32_10(drow + (uint32_t)(k0 >> 2) + 2 * cg + g, p.drop.seed_lo,
+                                          p.drop.seed_hi);
+        kbits = (w.w[0] >= p.drop.threshold ? 1u : 0u) | (w.w[1] >= p.drop.threshold ? 2u : 0u) |
+                (w.w[2] >= p.drop.threshold ? 4u : 0u) | (w.w[3] >= p.drop.threshold ? 8u : 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * cg + u;
+        const bool ok = !need_mask || (8 * cg + u <= lim);
+        const float ps = ok ? fast_exp2(fmaf(sacc[r], c, -lse2)) : 0.f;
+        float dp = dpacc[r];
+        if (DROPOUT) dp = ((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f;
+        dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dsum));
+      }
+    }
+    // dQ^T += K^T dS'^T: A = K^T read transposed from the tile, B = dS'^T from registers.
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint16_t* ak = kl + (16 * hf + tr_row) * TP + eb * 32 + tr_col;
+        dqa[eb] = mfma32x32x16(concat(lds_tr4(ak), lds_tr4(ak + 8 * TP)), dsb[hf], dqa[eb]);
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      ka[es] = kn[es];
+      va[es] = vn[es];
+    }
+  }
+
+  uint16_t* dqp = p.dq + b * p.sdq.b + h * p.sdq.h;
+  reduce_store<E>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, lds, wave, lane);
+}
+
+// Workgroup order: per head, the dK/dV and dQ blocks alternate, heaviest causal
+// blocks first; all blocks of a head sit on one XCD when the head count allows.
+template <int E, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdLds<E>::TOTAL];
+  const int bh_count = p.B * p.H;
+  int bh, slot;
+  if ((bh_count & 7) == 0) {
+    const int per_xcd = bh_count >> 3;
+    const int xcd = blockIdx.x & 7, sx = blockIdx.x >> 3;
+    slot = sx / per_xcd;
+    bh = xcd * per_xcd + (sx - slot * per_xcd);
+  } else {
+    slot = blockIdx.x / bh_count;
+    bh = blockIdx.x - slot * bh_count;
+  }
+  const int m = min(nkb, nqb);
+  bool dkdv;
+  int rank;
+  if (slot < 2 * m) {
+    dkdv = (slot & 1) == 0;
+    rank = slot >> 1;
+  } else {
+    dkdv = nkb > nqb;
+    rank = slot - m;
+  }
+  if (dkdv)
+    role_dkdv<E, CAUSAL, DROPOUT>(p, bh, rank, lds);
+  else
+    role_dq<E, CAUSAL, DROPOUT>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
 template <int E>
-hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
-  const int n_kblocks = (p.Sk + 127) / 128;
-  const dim3 grid((unsigned)n_kblocks * (unsigned)(p.B * p.H));
+hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
+  const int nkb = (p.Sk + 31) / 32, nqb = (p.Sq + 31) / 32;
+  const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
   if (causal) {
     if (dropout)
-      hipLaunchKernelGGL((bwd_main_kernel<E, true, true>), grid, dim3(256), 0, stream, p, n_kblocks);
+      hipLaunchKernelGGL((bwd_kernel<E, true, true>), grid, dim3(256), 0, stream, p, nkb, nqb);
     else
-      hipLaunchKernelGGL((bwd_main_kernel<E, true, false>), grid, dim3(256), 0, stream, p, n_kblocks);
+      hipLaunchKernelGGL((bwd_kernel<E, true, false>), grid, dim3(256), 0, stream, p, nkb, nqb);
   } else {
     if (dropout)
-      hipLaunchKernelGGL((bwd_main_kernel<E, false, true>), grid, dim3(256), 0, stream, p, n_kblocks);
+      hipLaunchKernelGGL((bwd_kernel<E, false, true>), grid, dim3(256), 0, stream, p, nkb, nqb);
     else
-      hipLaunchKernelGGL((bwd_main_kernel<E, false, false>), grid, dim3(256), 0, stream, p, n_kblocks);
+      hipLaunchKernelGGL((bwd_kernel<E, false, false>), grid, dim3(256), 0, stream, p, nkb, nqb);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_pre(const BwdParams& p, int E, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  const int rpb = 256 / (E / 8);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  if (E == 64)
-    hipLaunchKernelGGL(bwd_pre_kernel<64>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(bwd_pre_kernel<128>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_main(const BwdParams& p, int E, bool causal, bool dropout,
-                           hipStream_t stream) {
-  return E == 64 ? launch_main_t<64>(p, causal, dropout, stream)
-                 : launch_main_t<128>(p, causal, dropout, stream);
-}
-
-hipError_t launch_bwd_dq(const BwdParams& p, int E, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.B * p.H * p.Sq * (E / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256));
-  if (E == 64)
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream) {
+  return E == 64 ? launch_bwd_t<64>(p, causal, dropout, stream)
+                 : launch_bwd_t<128>(p, causal, dropout, stream);
 }
 
 }  // namespace sdpa14

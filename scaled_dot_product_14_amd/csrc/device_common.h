@@ -81,6 +81,18 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource over `bytes` bytes at `base`: 16-byte loads at offsets at
+// or past the end return zeros instead of touching memory (the range check of
+// the buffer unit), which replaces per-lane bounds branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // Round four floats to bf16 (nearest even) and pack them into 8 bytes.
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
   bf16x4 v;

@@ -8,18 +8,25 @@
 // dropout of the PyTorch PR "REDO of dropout support for mem eff" (absolute
 // index for the RNG stream).  The tiling is this file's own design for CDNA4.
 //
-// Workgroup: NW waves, each owning 32 query rows (BM = 32*NW rows per
-// workgroup).  Key/value tiles of BN rows are staged in LDS, shared by the
-// waves, with the next tile's global loads in flight while the current one is
-// consumed.
+// Workgroup: NQ x NS waves.  Each wave owns 32 query rows (a workgroup covers
+// BM = 32*NQ rows) and one of NS interleaved shares of the key tiles: at
+// iteration `it` the workgroup stages NS key/value tiles of BN rows in LDS and
+// wave (qs, ks) consumes tile it*NS + ks for query sub-tile qs.  The NS partial
+// softmax states (max, sum, O) of a query sub-tile are merged through LDS at
+// the end.  Splitting the keys shortens the longest chain of dependent tiles,
+// which is what limits small causal problems.
 //
 // Per wave and key tile:
 //   S^T = K_tile Q^T       v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
 //                          B = Q fragments held in registers for the whole loop.
 //                          Result layout: lane = query (l%32), registers run
 //                          over keys, four consecutive keys per register group.
-//   online softmax         every lane owns one query row; row statistics need
-//                          one exchange with lane l^32 (permlane32_swap).
+//   online softmax         every lane owns one query row; the row max needs one
+//                          exchange with lane l^32 (permlane32_swap).  The
+//                          reference max moves only when it grows by more than
+//                          2^8 (in the exp2 domain), so most tiles skip the
+//                          rescale of the O accumulator; probabilities then stay
+//                          below 2^8, harmless for fp32 sums and bf16 operands.
 //   dropout                the four consecutive keys of a register group are
 //                          exactly one Philox call.
 //   O^T += V^T P^T         A = V^T read transposed from the row-major V tile
@@ -27,8 +34,11 @@
 //                          S^T registers (converted to bf16): no LDS round trip
 //                          for P.  The contraction index is permuted
 //                          consistently on both operands.
-// The O^T accumulator keeps lane = query, so the rescale by exp(m_old - m_new)
-// is a per-lane multiply.
+// The O^T accumulator keeps lane = query, so every rescale is a per-lane multiply.
+//
+// Workgroup order: heaviest causal query tiles first, and the tiles of one head
+// on one XCD (workgroups are dealt to the 8 XCDs round-robin), so a head's K/V
+// stay in that XCD's L2.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,74 +46,100 @@ namespace sdpa14 {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.f;  // log2 units the reference max may lag
 
-template <int E, int NW, int BN, bool CAUSAL, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p, int n_qtiles) {
+// Maps a workgroup id to (head, rank); rank 0 is the heaviest query tile.
+__device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& rank) {
+  if ((bh_count & 7) == 0) {
+    const int per_xcd = bh_count >> 3;
+    const int xcd = bid & 7, slot = bid >> 3;
+    rank = slot / per_xcd;
+    bh = xcd * per_xcd + (slot - rank * per_xcd);
+  } else {
+    rank = bid / bh_count;
+    bh = bid - rank * bh_count;
+  }
+}
+
+template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT>
+__global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles) {
   static_assert(E % 32 == 0 && BN % 32 == 0, "tile shape");
-  constexpr int BM = NW * 32;
+  constexpr int NW = NQ * NS;
+  constexpr int BM = NQ * 32;
   constexpr int KP = E + 8;   // K tile pitch (elements): conflict-free 16-byte row reads
   constexpr int VP = E + 32;  // V tile pitch: conflict-free transposed reads
   constexpr int NT = NW * 64;
-  constexpr int CPR = E / 8;  // 16-byte chunks per row
-  constexpr int CHUNKS = BN * CPR;
+  constexpr int ROWS = NS * BN;  // key rows staged per iteration
+  constexpr int CPR = E / 8;     // 16-byte chunks per row
+  constexpr int CHUNKS = ROWS * CPR;
   constexpr int PER = (CHUNKS + NT - 1) / NT;
+  constexpr int NEB = E / 32;
+  constexpr int KV_BYTES = ROWS * (KP + VP) * 2;
+  constexpr int CMB_FLOATS = (NS - 1) * NQ * (NEB * 16 + 2) * 64;  // merge buffer
+  constexpr int LDS_BYTES = KV_BYTES > CMB_FLOATS * 4 ? KV_BYTES : CMB_FLOATS * 4;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[BN * VP];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  uint16_t* ks = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* vs = ks + ROWS * KP;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
+  const int qs = wave % NQ;  // query sub-tile of this wave
+  const int ksp = wave / NQ;  // key share of this wave
 
-  const int bh_count = p.B * p.H;
-  const int rank = blockIdx.x / bh_count;
-  const int bh = blockIdx.x - rank * bh_count;
-  // Causal tiles with more keys go first.
+  int bh, rank;
+  wg_to_tile(blockIdx.x, p.B * p.H, bh, rank);
   const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
-  const int q0 = qt * BM + wave * 32;  // first query row of this wave
-  const int qrow = q0 + l32;           // query row of this lane
+  const int q0 = qt * BM + qs * 32;  // first query row of this wave
+  const int qrow = q0 + l32;         // query row of this lane
 
   const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
   const uint16_t* kp = p.k + b * p.sk.b + h * p.sk.h;
   const uint16_t* vp = p.v + b * p.sv.b + h * p.sv.h;
 
-  // Q as the B operand of S^T = K Q^T: lane holds its row, e = 16*es + 8*g + 0..7.
-  bf16x8 qf[E / 16];
-#pragma unroll
-  for (int es = 0; es < E / 16; ++es)
-    qf[es] = (qrow < p.Sq) ? load_bf16x8(qp + (int64_t)qrow * p.sq.s + es * 16 + 8 * g)
-                           : zero_bf16x8();
-
   int kend = p.Sk;
   if (CAUSAL) kend = min(kend, min(p.Sq, (qt + 1) * BM));  // keys <= last row of the tile
   const int n_kt = (kend + BN - 1) / BN;
+  const int n_it = (n_kt + NS - 1) / NS;
+
+  // Q as the B operand of S^T = K Q^T: lane holds its row, e = 16*es + 8*g + 0..7.
+  // Rows past Sq read as zeros through the buffer range check.
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(qp, (uint32_t)(((int64_t)(p.Sq - 1) * p.sq.s + E) * 2));
+  bf16x8 qf[E / 16];
+#pragma unroll
+  for (int es = 0; es < E / 16; ++es)
+    qf[es] = __builtin_bit_cast(
+        bf16x8, buffer_load16(qr, (uint32_t)(((int64_t)qrow * p.sq.s + es * 16 + 8 * g) * 2)));
+
+  // K and V rows past kend read as zeros.
+  const uint32_t kbytes = (uint32_t)(((int64_t)(kend - 1) * p.sk.s + E) * 2);
+  const uint32_t vbytes = (uint32_t)(((int64_t)(kend - 1) * p.sv.s + E) * 2);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, kend > 0 ? kbytes : 0);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, kend > 0 ? vbytes : 0);
+  const uint32_t kstride = (uint32_t)(p.sk.s * 2), vstride = (uint32_t)(p.sv.s * 2);
 
   uint4 kreg[PER], vreg[PER];
-  auto load_tile = [&](int k0) {
+  auto load_rows = [&](int r0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      const int row = c / CPR, col = c - (c / CPR) * CPR;
-      const int key = k0 + row;
-      if (c < CHUNKS && key < p.Sk) {
-        kreg[i] = *reinterpret_cast<const uint4*>(kp + (int64_t)key * p.sk.s + col * 8);
-        vreg[i] = *reinterpret_cast<const uint4*>(vp + (int64_t)key * p.sv.s + col * 8);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
+      const uint32_t row = (uint32_t)(r0 + c / CPR), col16 = (uint32_t)(c % CPR) * 16u;
+      kreg[i] = buffer_load16(kr, row * kstride + col16);
+      vreg[i] = buffer_load16(vr, row * vstride + col16);
     }
   };
-  auto store_tile = [&]() {
+  auto store_rows = [&]() {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = tid + i * NT;
-      if (c < CHUNKS) {
-        const int row = c / CPR, col = c - (c / CPR) * CPR;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / CPR, col = c % CPR;
         *reinterpret_cast<uint4*>(ks + row * KP + col * 8) = kreg[i];
         *reinterpret_cast<uint4*>(vs + row * VP + col * 8) = vreg[i];
       }
@@ -114,107 +150,151 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p, int n_qtiles)
   // reads rows 4*g + (lane%16)/4 (+8), columns 16*((lane/16)%2) + 4*(lane%4).
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const uint16_t* kw = ks + ksp * BN * KP + l32 * KP + 8 * g;  // this wave's K rows
+  const uint16_t* vw = vs + ksp * BN * VP + tr_row * VP + tr_col;
 
-  f32x16 oacc[E / 32];
+  f32x16 oacc[NEB];
 #pragma unroll
-  for (int eb = 0; eb < E / 32; ++eb) oacc[eb] = zero16();
-  float m_run = -INFINITY;  // running max of scale*log2(e)*S for this row
-  float l_run = 0.f;        // this lane's share of the running row sum
+  for (int eb = 0; eb < NEB; ++eb) oacc[eb] = zero16();
+  float m_run = -INFINITY;  // reference max of scale*log2(e)*S for this row
+  float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
   const float c = p.scale_log2;
+  // Last visible key of this lane's row, for masking (top-left causal; ragged Sk).
+  const int key_limit = CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1;
 
   const int sk4 = (p.Sk + 3) >> 2;
   uint64_t drow = 0;
   if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
 
-  if (n_kt > 0) load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * BN;
+  load_rows(0);
+  for (int it = 0; it < n_it; ++it) {
     __syncthreads();
-    store_tile();
+    store_rows();
     __syncthreads();
-    if (kt + 1 < n_kt) load_tile(k0 + BN);
-    if (CAUSAL && k0 > q0 + 31) continue;  // tile lies above the diagonal for this wave
-
-    // S^T for BN keys x 32 queries.
-    f32x16 s[BN / 32];
+    if (it + 1 < n_it) load_rows((it + 1) * ROWS);
+    const int j = it * NS + ksp;
+    const int k0 = j * BN;
+    // Skip tiles past the key range and, when causal, above the diagonal.
+    const bool active = (j < n_kt) && (!CAUSAL || k0 <= q0 + 31);
+    if (active) {
+      // S^T for BN keys x 32 queries.
+      f32x16 s[BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      s[kb] = zero16();
+      for (int kb = 0; kb < BN / 32; ++kb) {
+        s[kb] = zero16();
 #pragma unroll
-      for (int es = 0; es < E / 16; ++es) {
-        const bf16x8 a = lds_bf16x8(ks + (kb * 32 + l32) * KP + es * 16 + 8 * g);
-        s[kb] = mfma32x32x16(a, qf[es], s[kb]);
+        for (int es = 0; es < E / 16; ++es)
+          s[kb] = mfma32x32x16(lds_bf16x8(kw + kb * 32 * KP + es * 16), qf[es], s[kb]);
       }
-    }
 
-    const bool need_mask = (CAUSAL && (k0 + BN - 1 > q0)) || (k0 + BN > p.Sk);
-    if (need_mask) {
+      if (k0 + BN - 1 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1)) {
+        const int lim = key_limit - k0 - 4 * g;  // key offset past which scores are hidden
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
+      }
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+      mx = pair_max(mx) * c;
+      // Move the reference max only when it grew by more than the slack; the
+      // decision is per row, the skip of the rescale is per wave.
+      const bool grow = mx > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[eb][r] *= alpha;
+      }
+
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // never -inf - -inf
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = (key < p.Sk) && (!CAUSAL || key <= qrow);
-          if (!ok) s[kb][r] = -INFINITY;
+          const float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
+          s[kb][r] = pv;
+          rs += pv;
+        }
+      l_run += rs;
+
+      if (DROPOUT) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int cg = 0; cg < 4; ++cg) {
+            // keys k0 + 32*kb + 8*cg + 4*g + 0..3: one Philox group
+            const uint32_t grp = (uint32_t)(k0 >> 2) + kb * 8 + cg * 2 + g;
+            const PhiloxOut w = philox4x32_10(drow + grp, p.drop.seed_lo, p.drop.seed_hi);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (w.w[t] < p.drop.threshold) s[kb][4 * cg + t] = 0.f;
+          }
+      }
+
+      // P as the B operand: 16-key step ks takes registers 8*(ks%2)..+7 of block
+      // ks/2, i.e. keys 16*ks + 8*(i/4) + 4*g + i%4 for element i.
+      bf16x8 pb[BN / 16];
+#pragma unroll
+      for (int ksx = 0; ksx < BN / 16; ++ksx)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[ksx][i] = (__bf16)s[ksx >> 1][8 * (ksx & 1) + i];
+
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int ksx = 0; ksx < BN / 16; ++ksx) {
+          const uint16_t* base = vw + ksx * 16 * VP + eb * 32;
+          oacc[eb] = mfma32x32x16(concat(lds_tr4(base), lds_tr4(base + 8 * VP)), pb[ksx],
+                                  oacc[eb]);
         }
     }
+  }
 
-    float mx = -INFINITY;
+  if (NS > 1) {
+    // Merge the key shares of each query sub-tile into the ksp == 0 wave.
+    float* cmb = reinterpret_cast<float*>(lds);
+    constexpr int SLOT = (NEB * 16 + 2) * 64;
+    __syncthreads();  // all waves are done with the K/V tiles
+    if (ksp > 0) {
+      float* dst = cmb + ((ksp - 1) * NQ + qs) * SLOT;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+      for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(s[kb][r], c, -m_new));
-        s[kb][r] = pv;
-        rs += pv;
-      }
-    l_run = l_run * alpha + rs;
-
-    if (DROPOUT) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) {
-          // keys k0 + 32*kb + 8*cg + 4*g + 0..3: one Philox group
-          const uint32_t grp = (uint32_t)(k0 >> 2) + kb * 8 + cg * 2 + g;
-          const PhiloxOut w = philox4x32_10(drow + grp, p.drop.seed_lo, p.drop.seed_hi);
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            if (w.w[t] < p.drop.threshold) s[kb][4 * cg + t] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r) dst[(eb * 16 + r) * 64 + lane] = oacc[eb][r];
+      dst[(NEB * 16) * 64 + lane] = m_run;
+      dst[(NEB * 16 + 1) * 64 + lane] = l_run;
     }
-
+    __syncthreads();
+    if (ksp == 0) {
 #pragma unroll
-    for (int eb = 0; eb < E / 32; ++eb)
+      for (int s2 = 1; s2 < NS; ++s2) {
+        const float* src = cmb + ((s2 - 1) * NQ + qs) * SLOT;
+        const float m_o = src[(NEB * 16) * 64 + lane];
+        const float l_o = src[(NEB * 16 + 1) * 64 + lane];
+        const float m_new = fmaxf(m_run, m_o);
+        const float a_s = fast_exp2(m_run - m_new);
+        const float a_o = fast_exp2(m_o - m_new);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[eb][r] *= alpha;
-
-    // P as the B operand: 16-key step ks takes registers 8*(ks%2)..+7 of block ks/2,
-    // i.e. keys 16*ks + 8*(i/4) + 4*g + i%4 for element i.
-    bf16x8 pb[BN / 16];
+        for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-    for (int ksx = 0; ksx < BN / 16; ++ksx)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[ksx][i] = (__bf16)s[ksx >> 1][8 * (ksx & 1) + i];
-
-#pragma unroll
-    for (int eb = 0; eb < E / 32; ++eb)
-#pragma unroll
-      for (int ksx = 0; ksx < BN / 16; ++ksx) {
-        const uint16_t* base = vs + (ksx * 16 + tr_row) * VP + eb * 32 + tr_col;
-        const bf16x8 a = concat(lds_tr4(base), lds_tr4(base + 8 * VP));
-        oacc[eb] = mfma32x32x16(a, pb[ksx], oacc[eb]);
+          for (int r = 0; r < 16; ++r)
+            oacc[eb][r] = oacc[eb][r] * a_s + src[(eb * 16 + r) * 64 + lane] * a_o;
+        l_run = l_run * a_s + l_o * a_o;
+        m_run = m_new;
       }
+    }
+    if (ksp != 0) return;
   }
 
   const float l_tot = pair_sum(l_run);
@@ -222,7 +302,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p, int n_qtiles)
   if (qrow < p.Sq) {
     uint16_t* op = p.o + b * p.so.b + h * p.so.h + (int64_t)qrow * p.so.s;
 #pragma unroll
-    for (int eb = 0; eb < E / 32; ++eb)
+    for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
         const int e = eb * 32 + 8 * cg + 4 * g;
@@ -234,22 +314,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p, int n_qtiles)
   }
 }
 
-template <int E, int NW, int BN>
+template <int E, int NQ, int NS, int BN>
 hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, hipStream_t stream) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NQ * 32;
   const int n_qtiles = (p.Sq + BM - 1) / BM;
   const dim3 grid((unsigned)n_qtiles * (unsigned)(p.B * p.H));
-  const dim3 block(NW * 64);
+  const dim3 block(NQ * NS * 64);
   if (causal) {
     if (dropout)
-      hipLaunchKernelGGL((fwd_kernel<E, NW, BN, true, true>), grid, block, 0, stream, p, n_qtiles);
+      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, true, true>), grid, block, 0, stream, p,
+                         n_qtiles);
     else
-      hipLaunchKernelGGL((fwd_kernel<E, NW, BN, true, false>), grid, block, 0, stream, p, n_qtiles);
+      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, true, false>), grid, block, 0, stream, p,
+                         n_qtiles);
   } else {
     if (dropout)
-      hipLaunchKernelGGL((fwd_kernel<E, NW, BN, false, true>), grid, block, 0, stream, p, n_qtiles);
+      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, false, true>), grid, block, 0, stream, p,
+                         n_qtiles);
     else
-      hipLaunchKernelGGL((fwd_kernel<E, NW, BN, false, false>), grid, block, 0, stream, p, n_qtiles);
+      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, false, false>), grid, block, 0, stream, p,
+                         n_qtiles);
   }
   return hipGetLastError();
 }
@@ -258,19 +342,23 @@ hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, hipStream
 
 hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
                       const TileChoice& tiles, hipStream_t stream) {
-  int nw = tiles.fwd_waves;
-  if (nw != 2 && nw != 4) {
-    // Fill the chip: prefer 4-wave workgroups unless that leaves fewer than two
-    // workgroups per compute unit.
+  // Shape: 4 query sub-tiles sharing each key tile when there are enough
+  // 128-row tiles to give every compute unit two workgroups; otherwise two
+  // query sub-tiles with the keys split in two, for a shorter critical path.
+  int shape = tiles.fwd_shape;  // 1: NQ=4,NS=1   2: NQ=2,NS=2   3: NQ=1,NS=4
+  if (shape < 1 || shape > 3) {
     const long wg4 = (long)((p.Sq + 127) / 128) * p.B * p.H;
-    nw = (wg4 >= 512) ? 4 : 2;
+    shape = (wg4 >= 512) ? 1 : 2;
   }
   if (E == 64) {
-    return nw == 4 ? launch_fwd_t<64, 4, 64>(p, causal, dropout, stream)
-                   : launch_fwd_t<64, 2, 64>(p, causal, dropout, stream);
+    if (shape == 1) return launch_fwd_t<64, 4, 1, 64>(p, causal, dropout, stream);
+    if (shape == 2) return launch_fwd_t<64, 2, 2, 64>(p, causal, dropout, stream);
+    return launch_fwd_t<64, 1, 4, 64>(p, causal, dropout, stream);
   }
-  return nw == 4 ? launch_fwd_t<128, 4, 64>(p, causal, dropout, stream)
-                 : launch_fwd_t<128, 2, 64>(p, causal, dropout, stream);
+  // One query sub-tile with four key shares needs more registers than head dim
+  // 128 leaves; it falls back to two by two.
+  if (shape == 1) return launch_fwd_t<128, 4, 1, 64>(p, causal, dropout, stream);
+  return launch_fwd_t<128, 2, 2, 64>(p, causal, dropout, stream);
 }
 
 }  // namespace sdpa14

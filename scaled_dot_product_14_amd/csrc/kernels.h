@@ -36,8 +36,6 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   const float* lse;  // contiguous [B, H, Sq]
-  float* delta;      // workspace: D = rowsum(dO * O), contiguous [B, H, Sq]
-  float* dq_acc;     // workspace: fp32 dQ, contiguous [B, H, Sq, E]
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Sq, Sk;
   float scale;       // softmax scale
@@ -53,15 +51,13 @@ struct MaskParams {
 
 // Tile choices the launchers take; 0 lets the launcher decide.
 struct TileChoice {
-  int fwd_waves;  // waves per forward workgroup (32 query rows each)
+  int fwd_shape;  // forward workgroup: 1 = 4 query sub-tiles, 2 = 2 sub-tiles x 2 key
+                  // shares, 3 = 1 sub-tile x 4 key shares (32 query rows per sub-tile)
 };
 
 hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
                       const TileChoice& tiles, hipStream_t stream);
-hipError_t launch_bwd_pre(const BwdParams& p, int E, hipStream_t stream);
-hipError_t launch_bwd_main(const BwdParams& p, int E, bool causal, bool dropout,
-                           hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdParams& p, int E, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream);
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream);
 
 }  // namespace sdpa14

@@ -1,6 +1,5 @@
 // C ABI of libsdpa14: argument validation, stride resolution, the Philox
-// state handed from forward to backward, workspace sizing, launches and
-// optional event timing.  The compute itself lives in fwd.hip / bwd.hip.
+// state handed from forward to backward, launches and optional event timing.  The compute itself lives in fwd.hip / bwd.hip.
 //
 // The forward returns (out, lse, seed, offset) and the backward consumes
 // (seed, offset), as in the sdpfa_fwd / sdpfa_bwd pair of the nvFuser PR "DID
@@ -90,6 +89,11 @@ bool same_shape(const Desc& a, const Desc& b) {
   return a.B == b.B && a.H == b.H && a.S == b.S && a.E == b.E;
 }
 
+// Kernels read rows of one (batch, head) slice through 32-bit buffer offsets.
+bool slice_ok(const Desc& t) {
+  return (t.S - 1) * t.st.s * 2 + t.E * 2 < (int64_t(1) << 31);
+}
+
 int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
   if (q.B != k.B || q.B != v.B || q.H != k.H || q.H != v.H)
     return fail(SDPA_ERR_INVALID, "q, k, v disagree on batch or heads");
@@ -100,8 +104,10 @@ int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
   if (q.E != 64 && q.E != 128)
     return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not supported (64 or 128)",
                 (long long)q.E);
-  const int64_t grid_f = q.B * q.H * ((q.S + 31) / 32);
+  const int64_t grid_f = q.B * q.H * ((q.S + 31) / 32 + (k.S + 31) / 32);
   if (grid_f > kMaxGrid) return fail(SDPA_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (!slice_ok(q) || !slice_ok(k) || !slice_ok(v))
+    return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice spans 2 GiB or more");
   return SDPA_OK;
 }
 
@@ -135,8 +141,6 @@ DropoutParams make_dropout(double p, uint64_t seed, uint64_t offset) {
 uint64_t offset_advance(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
   return (uint64_t)B * (uint64_t)H * (uint64_t)Sq * (uint64_t)((Sk + 3) / 4);
 }
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- event timing -----------------------------------------------------------
 struct Profiler {
@@ -180,7 +184,7 @@ int hip_status(hipError_t err, const char* what) {
 TileChoice tile_choice() {
   static const TileChoice tc = [] {
     TileChoice t{0};
-    if (const char* s = getenv("SDPA14_FWD_WAVES")) t.fwd_waves = atoi(s);
+    if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
     return t;
   }();
   return tc;
@@ -242,18 +246,10 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
   return hip_status(err, "forward launch");
 }
 
-size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t E) {
-  (void)Sk;
-  if (B < 1 || H < 1 || Sq < 1 || E < 1) return 0;
-  const size_t rows = (size_t)B * (size_t)H * (size_t)Sq;
-  return align256(rows * sizeof(float)) + align256(rows * (size_t)E * sizeof(float));
-}
-
 int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
              const sdpa_tensor* v, const sdpa_tensor* out, const float* lse, double dropout_p,
              int is_causal, uint64_t seed, uint64_t offset, double scale, const sdpa_tensor* dq,
-             const sdpa_tensor* dk, const sdpa_tensor* dv, void* workspace,
-             size_t workspace_bytes, sdpa_stream_t stream) {
+             const sdpa_tensor* dk, const sdpa_tensor* dv, sdpa_stream_t stream) {
   Desc ddo, dqi, dki, dvi, dout_i, dqo, dko, dvo;
   int rc;
   if ((rc = check_tensor(dout, "dout", &ddo))) return rc;
@@ -270,18 +266,14 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   if (!same_shape(dqi, dqo)) return fail(SDPA_ERR_INVALID, "dq must have q's shape");
   if (!same_shape(dki, dko)) return fail(SDPA_ERR_INVALID, "dk must have k's shape");
   if (!same_shape(dvi, dvo)) return fail(SDPA_ERR_INVALID, "dv must have v's shape");
+  if (!slice_ok(ddo) || !slice_ok(dout_i))
+    return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice spans 2 GiB or more");
   if (lse == nullptr) return fail(SDPA_ERR_INVALID, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "lse is not 4-byte aligned");
   if ((rc = check_dropout(dropout_p))) return rc;
   float sc;
   if ((rc = resolve_scale(scale, dqi.E, &sc))) return rc;
-  const size_t need = sdpa_bwd_workspace_size(dqi.B, dqi.H, dqi.S, dki.S, dqi.E);
-  if (workspace == nullptr) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(SDPA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
 
   BwdParams p;
   p.q = dqi.ptr;
@@ -293,9 +285,6 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   p.dk = const_cast<uint16_t*>(dko.ptr);
   p.dv = const_cast<uint16_t*>(dvo.ptr);
   p.lse = lse;
-  const size_t rows = (size_t)dqi.B * dqi.H * dqi.S;
-  p.delta = static_cast<float*>(workspace);
-  p.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * sizeof(float)));
   p.sq = dqi.st;
   p.sk = dki.st;
   p.sv = dvi.st;
@@ -315,13 +304,9 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  hipError_t err = timed_launch(SDPA_KERNEL_BWD_PRE, st, [&] { return launch_bwd_pre(p, E, st); });
-  if (err != hipSuccess) return hip_status(err, "backward preprocess launch");
-  err = timed_launch(SDPA_KERNEL_BWD_MAIN, st,
-                     [&] { return launch_bwd_main(p, E, causal, drop, st); });
-  if (err != hipSuccess) return hip_status(err, "backward main launch");
-  err = timed_launch(SDPA_KERNEL_BWD_DQ, st, [&] { return launch_bwd_dq(p, E, st); });
-  return hip_status(err, "backward dQ launch");
+  const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
+                                      [&] { return launch_bwd(p, E, causal, drop, st); });
+  return hip_status(err, "backward launch");
 }
 
 void sdpa_set_rng_state(uint64_t seed, uint64_t offset) {

@@ -96,26 +96,23 @@ def test_forward_rejects_bad_arguments(lib, kw, code, needle):
     assert bnd.sdpa_get_rng_state() == (1234, 99)
 
 
-def _bwd(lib, ws=FAKE, ws_bytes=None, **over):
+def _bwd(lib, **over):
     t = {n: over.get(n) or _t() for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
-    need = lib.sdpa_bwd_workspace_size(1, 2, 128, 128, 64)
-    ws_bytes = need if ws_bytes is None else ws_bytes
     return lib.sdpa_bwd(*(ctypes.byref(t[n]) for n in ("dout", "q", "k", "v", "out")),
                         over.get("lse", FAKE), over.get("p", 0.0), 1, 0, 0,
                         over.get("scale", math.nan),
-                        *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")), ws, ws_bytes, None)
+                        *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")), None)
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(ws=0), bnd.SDPA_ERR_WORKSPACE),
-    (dict(ws=FAKE + 16), bnd.SDPA_ERR_WORKSPACE),
-    (dict(ws_bytes=1000), bnd.SDPA_ERR_WORKSPACE),
     (dict(dk=_t(S=64)), bnd.SDPA_ERR_INVALID),
     (dict(dq=_t(S=64)), bnd.SDPA_ERR_INVALID),
     (dict(dout=_t(E=128)), bnd.SDPA_ERR_INVALID),
     (dict(lse=0), bnd.SDPA_ERR_INVALID),
     (dict(p=1.5), bnd.SDPA_ERR_INVALID),
     (dict(dv=_t(dtype=3)), bnd.SDPA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), bnd.SDPA_ERR_INVALID),
+    (dict(out=_t(stride=(2 * 128 * 64, 128 * 64, 64, 2))), bnd.SDPA_ERR_UNSUPPORTED),
 ])
 def test_backward_rejects_bad_arguments(lib, kw, code):
     bnd.sdpa_set_rng_state(5, 6)
@@ -124,13 +121,11 @@ def test_backward_rejects_bad_arguments(lib, kw, code):
     assert bnd.sdpa_get_rng_state() == (5, 6)
 
 
-def test_workspace_size():
-    # D (fp32 [B,H,Sq]) and dQ_acc (fp32 [B,H,Sq,E]), each 256-byte aligned.
-    assert sdpa.sdpa_bwd_workspace_size(2, 12, 1024, 1024, 64) == 2 * 12 * 1024 * 4 + 2 * 12 * 1024 * 64 * 4
-    rows = 4 * 16 * 1000
-    assert sdpa.sdpa_bwd_workspace_size(4, 16, 1000, 1000, 64) == rows * 4 + rows * 64 * 4
-    assert sdpa.sdpa_bwd_workspace_size(1, 1, 3, 5, 64) == 256 + 768
-    assert sdpa.sdpa_bwd_workspace_size(0, 1, 3, 5, 64) == 0
+def test_slice_too_large_is_unsupported(lib):
+    # Rows of one (batch, head) slice must sit within 2 GiB (32-bit buffer offsets).
+    big = _t(B=1, H=1, S=2**20, E=64, stride=(2**20 * 2048, 2**20 * 2048, 2048, 1))
+    rc = _fwd(lib, q=big, k=_t(B=1, H=1), v=_t(B=1, H=1), out=_t(B=1, H=1, S=2**20, stride=(2**20 * 2048, 2**20 * 2048, 2048, 1)))
+    assert rc == bnd.SDPA_ERR_UNSUPPORTED and "2 GiB" in _err(lib)
 
 
 def test_rng_state_roundtrip():
