@@ -23,6 +23,7 @@ for calibrating hardware byte counters).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -50,6 +51,33 @@ def parse():
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {
+    "fwd": ["fwd.hip", "device_common.h", "philox.h", "kernels.h"],
+    "bwd": ["bwd.hip", "device_common.h", "philox.h", "kernels.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    """sha256 over the sources a kernel is built from (to tell stale counters)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "scaled_dot_product_14_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == source_hash(kernel) else None
 
 
 def copy_calibration(nbytes: int, steps: int):
@@ -126,8 +154,7 @@ def main():
         copy_calibration(args.copy_bytes, args.steps)
         return
 
-    root = os.path.dirname(os.path.abspath(__file__))
-    sys.path.insert(0, root)
+    sys.path.insert(0, ROOT)
     import scaled_dot_product_14_amd as sdpa
     import workloads
 
@@ -197,7 +224,7 @@ def main():
     dk_ = kern[dominant]
     roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
-            "traffic": None}
+            "traffic": measured_traffic(w.name, dominant)}
 
     result = {
         "metric": METRIC,
