@@ -63,7 +63,7 @@ typedef enum sdpa_status {
   SDPA_OK = 0,
   SDPA_ERR_INVALID = 1,     /* null pointer, shape mismatch, E != Ev, p not in [0,1), bad scale */
   SDPA_ERR_UNSUPPORTED = 2, /* dtype, head dim, stride or alignment this build does not handle */
-  SDPA_ERR_WORKSPACE = 3,   /* reserved (no call takes a workspace) */
+  SDPA_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or smaller than required */
   SDPA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } sdpa_status;
 
@@ -98,15 +98,24 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
  *   seed, offset        the values sdpa_fwd returned; ignored when dropout_p == 0.
  *   dq, dk, dv          bf16 outputs shaped like q, k, v (any supported strides);
  *                       they must not overlap the inputs.
- * One kernel runs on `stream`.  It needs no workspace: D = rowsum(dO * O) is
- * formed on the fly, dK/dV come from key-block workgroups and dQ from
- * query-block workgroups (no atomics), so all three are bitwise reproducible.
+ *   workspace           device scratch owned by the caller, 256-byte aligned, at
+ *                       least sdpa_bwd_workspace_size(B, H, Sq) bytes; it must not
+ *                       overlap any tensor and may be reused once the call's work
+ *                       on `stream` is done.  Its contents need no initialization.
+ * Two kernels run on `stream`: a row pass storing D = rowsum(dO * O) and the
+ * row's LSE in base 2 into the workspace, then the main kernel, where dK/dV come
+ * from key-block workgroups and dQ from query-block workgroups (no atomics), so
+ * all three are bitwise reproducible.
  */
 int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
              const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
              double dropout_p, int is_causal, uint64_t seed, uint64_t offset, double scale,
              const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
-             sdpa_stream_t stream);
+             void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
+
+/* Workspace bytes sdpa_bwd needs for B*H*Sq query rows (8 per row, rounded up to
+ * 256); 0 when a size is not positive. */
+size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq);
 
 /* Library-global Philox state (process wide, mutex guarded).  Default (0, 0). */
 void sdpa_set_rng_state(uint64_t seed, uint64_t offset);

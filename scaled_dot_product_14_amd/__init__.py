@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     describe,
     load_library,
     sdpa_bwd,
+    sdpa_bwd_workspace_size,
     sdpa_debug_dropout_mask,
     sdpa_fwd,
     sdpa_get_rng_state,

@@ -27,7 +27,7 @@ KERNEL_FWD = 0
 KERNEL_BWD = 1
 
 EXPORTED = (
-    "sdpa_fwd", "sdpa_bwd", "sdpa_set_rng_state",
+    "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_set_rng_state",
     "sdpa_get_rng_state", "sdpa_status_string", "sdpa_last_error",
     "sdpa_debug_dropout_mask", "sdpa_profile_enable", "sdpa_profile_read",
 )
@@ -66,8 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.sdpa_fwd.restype = ctypes.c_int
     lib.sdpa_bwd.argtypes = [P, P, P, P, P, ctypes.c_void_p, ctypes.c_double, ctypes.c_int,
                              ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, P, P, P,
-                             ctypes.c_void_p]
+                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.sdpa_bwd.restype = ctypes.c_int
+    lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_set_rng_state.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
     lib.sdpa_set_rng_state.restype = None
     lib.sdpa_get_rng_state.argtypes = [u64p, u64p]
@@ -148,18 +150,32 @@ def sdpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dropout_p: float
     return out, lse, seed.value, offset.value
 
 
+def sdpa_bwd_workspace_size(B: int, H: int, Sq: int) -> int:
+    """Bytes of device workspace ``sdpa_bwd`` needs for ``B*H*Sq`` query rows."""
+    return int(load_library().sdpa_bwd_workspace_size(int(B), int(H), int(Sq)))
+
+
 def sdpa_bwd(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int,
-             offset: int, scale=None, dq=None, dk=None, dv=None):
-    """Backward: returns ``(dq, dk, dv)`` laid out like q, k, v."""
+             offset: int, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward: returns ``(dq, dk, dv)`` laid out like q, k, v.
+
+    ``workspace`` (optional) is a device uint8 tensor of at least
+    ``sdpa_bwd_workspace_size(B, H, Sq)`` bytes; one is allocated when omitted.
+    """
     lib = load_library()
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    B, H, Sq = q.shape[0], q.shape[1], q.shape[2]
+    if workspace is None:
+        workspace = torch.empty(max(lib.sdpa_bwd_workspace_size(B, H, Sq), 256),
+                                dtype=torch.uint8, device=q.device)
     descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                           float(dropout_p), int(bool(is_causal)), int(seed), int(offset),
                           _scale_arg(scale), *(ctypes.byref(d) for d in descs[5:]),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream(q.device))
     _check(rc)
     return dq, dk, dv

@@ -5,26 +5,32 @@
 // for SDPA"; dropout regenerates the forward's mask from (seed, offset) and the
 // absolute element index (PyTorch PR "REDO of dropout support for mem eff").
 //
-// One launch, two workgroup roles, no atomics and no workspace.  Each
-// workgroup stages the tiles it streams in LDS with row-contiguous loads (every
-// 8 lanes read one 128-byte row), and two waves share every staged tile; the
-// vector-memory path, not the matrix cores, is what limits this pass.
+// Two launches, no atomics:
 //
-//   dK/dV role  a 64-key block: waves (sb, qs), sb = 32-key sub-block,
-//               qs = which of the two 32-row query tiles of an iteration.
-//               Each wave keeps its sub-block's K and V fragments and its dK^T,
-//               dV^T accumulators in registers.  Per query tile:
-//                 S = Q K^T, dPd = dO V^T          (lane = key, registers = rows)
-//                 Ps = scale * exp(S*scale - LSE)  (masked; dropout kept/scaled)
-//                 dS' = Ps * (dP - D),  D_i = rowsum(dO * O) from the staged tiles
-//                 dV^T += dO^T Pd, dK^T += Q^T dS' (dO^T, Q^T read transposed)
-//               The two query-tile waves of a sub-block are summed at the end.
-//   dQ role     a 64-row block: waves (qsb, ks), qsb = 32-row sub-block, ks =
-//               which of the two 32-key tiles of an iteration.  Each wave keeps
-//               its rows' Q and dO fragments, D and LSE in registers.  Per key
-//               tile: S^T = K Q^T, dP^T = V dO^T (lane = row), dS'^T as above,
-//               dQ^T += K^T dS'^T with K^T read transposed.  The two key-tile
-//               waves of a sub-block are summed at the end.
+//   prep        one pass over the rows: D_i = rowsum(dO * O) and the row's
+//               LSE*log2(e) - log2(scale), stored as a float pair per row in
+//               the caller's workspace.
+//   main        two workgroup roles.
+//     dK/dV role  a 64-key block: waves (sb, qs), sb = 32-key sub-block, qs =
+//                 which of the two 32-row query tiles of an iteration.  Each
+//                 wave keeps its sub-block's K and V fragments and its dK^T,
+//                 dV^T accumulators in registers.  Per query tile:
+//                   S = Q K^T, dPd = dO V^T          (lane = key, registers = rows)
+//                   Ps = scale * exp(S*scale - LSE)  (masked; dropout kept/scaled)
+//                   dS' = Ps * (dP - D)
+//                   dV^T += dO^T Pd, dK^T += Q^T dS' (dO^T, Q^T read transposed)
+//     dQ role     a 64-row block: waves (qsb, ks), qsb = 32-row sub-block, ks =
+//                 which of the two 32-key tiles of an iteration.  Each wave
+//                 keeps its rows' Q and dO fragments, D and LSE in registers.
+//                 Per key tile: S^T = K Q^T, dP^T = V dO^T (lane = row), dS'^T
+//                 as above, dQ^T += K^T dS'^T with K^T read transposed.
+//               The tiles a workgroup streams (Q and dO, or K and V) go straight
+//               from memory to LDS (buffer loads with the LDS destination), into
+//               a ring of three stages filled two iterations ahead, so neither
+//               registers nor VALU work are spent on staging and the memory
+//               latency is covered by two iterations of math.  The two waves of
+//               a sub-block are summed through LDS at the end; each finalizes
+//               half of the outputs.
 //
 // Both roles recompute S and dP, so the backward does 7 products of 2*E flops
 // per visible score element (5 are counted).  In exchange dQ needs neither
@@ -38,55 +44,110 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// A staged tile holds 32 rows of E bf16, 2E bytes per row, no padding.  The
+// 16-byte chunk c of row r sits at chunk position c ^ tile_swz(r).  The
+// permutation keeps the two read patterns free of LDS bank conflicts: the
+// row-per-lane 16-byte reads (16 consecutive rows, one chunk) and the
+// transposed 8-byte reads (4 consecutive rows x 4 aligned chunks).
+template <int E>
+__device__ __forceinline__ int tile_swz(int r) {
+  return E == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
 template <int E>
 struct BwdCfg {
-  static constexpr int TP = E + 8;               // staged tile pitch (elements)
-  static constexpr int TILE = 32 * TP;            // elements per staged 32-row tile
-  static constexpr int CPR = E / 8;               // 16-byte chunks per row
-  static constexpr int CPT = 32 * CPR / 256;      // chunks per thread per tile (256 threads)
-  static constexpr int NEB = E / 32;
-  static constexpr int NES = E / 16;
-  // dK/dV role: 6 tiles (Q, dO, O for two query tiles) + per-wave D/LSE rows.
-  static constexpr int A_BYTES = 6 * TILE * 2 + 4 * 64 * 4;
-  // End-of-block reduction: two fp32 accumulator sets (dK^T, dV^T) per sub-block.
-  static constexpr int RED_BYTES = 2 * 2 * NEB * 16 * 64 * 4;
-  static constexpr int TOTAL = (A_BYTES > RED_BYTES ? A_BYTES : RED_BYTES);
+  static constexpr int NES = E / 16;  // 16-wide contraction steps over E
+  static constexpr int NEB = E / 32;  // 32-wide output blocks over E
+  static constexpr int CPR = E / 8;   // 16-byte chunks per row
+  static constexpr int ROW_B = 2 * E;
+  static constexpr int TILE_B = 32 * ROW_B;
+  static constexpr int NLD = TILE_B / (256 * 16);  // LDS-DMA loads per thread per tile
+  static constexpr int DL_B = 64 * 8;              // (D, L) of the pair's 64 rows
+  static constexpr int STAGE_A = 4 * TILE_B + DL_B;  // Q, Q', dO, dO', (D, L)
+  static constexpr int STAGE_B = 4 * TILE_B;         // K, K', V, V'
+  static constexpr int NSTAGE = 3;
+  static constexpr int NPAIR_A = 4 * NLD + 1;  // loads per thread per stage, dK/dV role
+  static constexpr int NPAIR_B = 4 * NLD;      // loads per thread per stage, dQ role
+  static constexpr int RED_B = 4 * NEB * 16 * 64 * 4;  // end-of-block exchange
+  static constexpr int LDS_B = NSTAGE * STAGE_A;
+  static_assert(STAGE_A >= STAGE_B && LDS_B >= RED_B, "LDS budget");
 };
 
-// Adds, for each sub-block, the accumulator of the wave with `second` set into
-// the wave without it, then that wave stores bf16 rows (C layout: lane = output
-// row row0 + l32, register r = column 32*eb + 8*(r/4) + 4*g + r%4).
+// s_waitcnt with vmcnt <= VM and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt in 6:4 left at its maximum, lgkmcnt in 11:8).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier of the LDS ring.  Each wave first waits until at most VM
+// of its loads are in flight (the older ones, which fill the next stage, have
+// landed in LDS) and its LDS reads have returned.  The empty asm statements
+// keep the compiler from moving LDS accesses across the barrier.
+template <int VM>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  wait_vm_lgkm0<VM>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte buffer load per lane into LDS: lane l writes lds_wave + 16*l.
+// lds_wave must be wave-uniform.  Out-of-range offsets deliver zeros.  Issued
+// from inline assembly so that the compiler's wait bookkeeping does not tie
+// later LDS reads of other stages to these loads; the ring barrier waits for
+// them explicitly.  M0 carries the LDS address (the compiler sets M0 afresh
+// before each of its own uses).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is a reserved register
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_wave,
+                                      uint32_t voff) {
+  const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voff), "s"(r)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows,
+                                                            int64_t stride, int E) {
+  return make_rsrc(base, rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * stride + E) * 2) : 0u);
+}
+
+// Per-thread part of a tile load: load k of thread tid fills slot k*256 + tid,
+// i.e. row slot/CPR at chunk position slot%CPR, which holds the global chunk
+// (slot%CPR) ^ tile_swz(row).  Returns the byte offset from the tile's first row.
 template <int E>
-__device__ __forceinline__ void pair_reduce_store(const f32x16 (&acc)[E / 32], float mul,
-                                                  uint16_t* dst, int64_t stride, int row0,
-                                                  int limit, float* red, int slot, bool second,
-                                                  int lane) {
-  constexpr int NEB = E / 32;
-  float* buf = red + slot * (NEB * 16 * 64);
-  if (second) {
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) buf[(eb * 16 + r) * 64 + lane] = acc[eb][r];
-  }
-  __syncthreads();
-  if (!second) {
-    const int row = row0 + (lane & 31);
-    const int g = lane >> 5;
-    if (row < limit) {
-#pragma unroll
-      for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) {
-          float v[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            v[t] = (acc[eb][4 * cg + t] + buf[(eb * 16 + 4 * cg + t) * 64 + lane]) * mul;
-          *reinterpret_cast<uint2*>(dst + (int64_t)row * stride + eb * 32 + 8 * cg + 4 * g) =
-              pack_bf16x4(v[0], v[1], v[2], v[3]);
-        }
-    }
-  }
+__device__ __forceinline__ uint32_t dma_src_offset(int k, int tid, int64_t row_stride) {
+  constexpr int CPR = E / 8;
+  const int slot = k * 256 + tid;
+  const int row = slot / CPR, pos = slot % CPR;
+  return (uint32_t)row * (uint32_t)(row_stride * 2) + (uint32_t)((pos ^ tile_swz<E>(row)) * 16);
+}
+
+// LDS byte offset, within a tile, of the chunk holding elements 8c .. 8c+7 of row r.
+template <int E>
+__device__ __forceinline__ int chunk_off(int r, int c) {
+  return r * (2 * E) + ((c ^ tile_swz<E>(r)) << 4);
+}
+
+// LDS byte offset, within a tile, of elements e .. e+3 of row r (e % 4 == 0),
+// the 8 bytes one lane addresses in a transposed read.
+template <int E>
+__device__ __forceinline__ int tr_off(int r, int e) {
+  return r * (2 * E) + (((e >> 3) ^ tile_swz<E>(r)) << 4) + ((e & 4) << 1);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_at(const unsigned char* base, int off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(const unsigned char* tile, int o0, int o1) {
+  return concat(lds_tr4(reinterpret_cast<const uint16_t*>(tile + o0)),
+                lds_tr4(reinterpret_cast<const uint16_t*>(tile + o1)));
 }
 
 // Dropout keep bits for the dK/dV role.  The lane holds key `key` (key % 4 ==
@@ -110,9 +171,52 @@ __device__ __forceinline__ uint32_t keep_bits_for_key(const DropoutParams& d, in
          (((n3 >> t) & 1) << 3);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows,
-                                                            int64_t stride, int E) {
-  return make_rsrc(base, rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * stride + E) * 2) : 0u);
+// End-of-block exchange between the two waves of a sub-block.  Each wave
+// holds NEB accumulator blocks (C layout: lane = output row row0 + l32,
+// register r of block eb = column 32*eb + 8*(r/4) + 4*g + r%4).  The wave with
+// `upper` set finalizes blocks NEB/2 .. NEB-1, the other blocks 0 .. NEB/2-1.
+// exchange_put writes the half the partner finalizes into this wave's slot;
+// after a barrier, exchange_finish adds the partner's slot, scales by mul and
+// stores bf16 rows below `limit`.
+template <int E>
+__device__ __forceinline__ void exchange_put(const f32x16 (&acc)[E / 32], float* red, int slot,
+                                             bool upper, int lane) {
+  constexpr int HALF = E / 64;
+  f32x4* buf = reinterpret_cast<f32x4*>(red + slot * (HALF * 16 * 64));
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const int eb = upper ? i : HALF + i;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      f32x4 v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = acc[eb][4 * cg + t];
+      buf[(i * 4 + cg) * 64 + lane] = v;
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], float mul,
+                                                uint16_t* dst, int64_t stride, int row0,
+                                                int limit, const float* red, int partner_slot,
+                                                bool upper, int lane) {
+  constexpr int HALF = E / 64;
+  const f32x4* buf = reinterpret_cast<const f32x4*>(red + partner_slot * (HALF * 16 * 64));
+  const int row = row0 + (lane & 31);
+  const int g = lane >> 5;
+  if (row >= limit) return;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const int eb = upper ? HALF + i : i;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      const f32x4 o = buf[(i * 4 + cg) * 64 + lane];
+      *reinterpret_cast<uint2*>(dst + (int64_t)row * stride + eb * 32 + 8 * cg + 4 * g) =
+          pack_bf16x4((acc[eb][4 * cg + 0] + o[0]) * mul, (acc[eb][4 * cg + 1] + o[1]) * mul,
+                      (acc[eb][4 * cg + 2] + o[2]) * mul, (acc[eb][4 * cg + 3] + o[3]) * mul);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -120,23 +224,21 @@ template <int E, bool CAUSAL, bool DROPOUT>
 __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                                           unsigned char* lds) {
   using C = BwdCfg<E>;
-  constexpr int NES = C::NES, NEB = C::NEB, TP = C::TP, CPR = C::CPR, CPT = C::CPT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
+  constexpr int ST_Q = 0, ST_DO = 2 * TILE_B, ST_DL = 4 * TILE_B;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int sb = wave & 1, qs = wave >> 1;
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int kb0 = kblk * 64;
   const int kbs = kb0 + 32 * sb;  // first key of this wave's sub-block
   const int key = kbs + l32;
   const float c = p.scale_log2;
-  const float lsc = __log2f(p.scale);
 
-  const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
-  const uint16_t* op = p.o + b * p.so.b + h * p.so.h;
-  const float* lsep = p.lse + (int64_t)bh * p.Sq;
-  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qp, p.Sq, p.sq.s, E);
-  const __amdgpu_buffer_rsrc_t rdo = rows_rsrc(dop, p.Sq, p.sdo.s, E);
-  const __amdgpu_buffer_rsrc_t ro = rows_rsrc(op, p.Sq, p.so.s, E);
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, E);
+  const __amdgpu_buffer_rsrc_t rdo =
+      rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, E);
+  const __amdgpu_buffer_rsrc_t rdl = make_rsrc(p.dl + (int64_t)bh * p.Sq * 2, (uint32_t)p.Sq * 8u);
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
   const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
 
@@ -159,141 +261,161 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const int nqt = (p.Sq + 31) / 32;
   const int t0 = CAUSAL ? min(kb0 / 32, nqt) : 0;
   const int n_it = (nqt - t0 + 1) / 2;
-  uint16_t* tiles = reinterpret_cast<uint16_t*>(lds);  // [query tile slot][Q, dO, O]
-  float* rv = reinterpret_cast<float*>(lds + 6 * C::TILE * 2) + wave * 64;  // D[32], LSE2[32]
 
-  // Row-contiguous staging: thread tid moves chunks tid + 256*k of each tile.
-  uint4 stg[6][CPT];
-  auto load_pair = [&](int it) {
+  // Stage it % 3 of the ring holds query tiles t0 + 2*it and t0 + 2*it + 1.
+  uint32_t oq[NLD], odo[NLD];
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) {
+    oq[k] = dma_src_offset<E>(k, tid, p.sq.s);
+    odo[k] = dma_src_offset<E>(k, tid, p.sdo.s);
+  }
+  auto issue = [&](int it) {
+    unsigned char* st = lds + (it % 3) * C::STAGE_A;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int row0 = (t0 + 2 * it + half) * 32;
+      const uint32_t row0 = (uint32_t)((t0 + 2 * it + half) * 32);
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const int cidx = tid + 256 * k;
-        const uint32_t row = (uint32_t)(row0 + cidx / CPR), col16 = (uint32_t)(cidx % CPR) * 16u;
-        stg[3 * half + 0][k] = buffer_load16(rq, row * (uint32_t)(p.sq.s * 2) + col16);
-        stg[3 * half + 1][k] = buffer_load16(rdo, row * (uint32_t)(p.sdo.s * 2) + col16);
-        stg[3 * half + 2][k] = buffer_load16(ro, row * (uint32_t)(p.so.s * 2) + col16);
+      for (int k = 0; k < NLD; ++k) {
+        dma16(rq, st + ST_Q + half * TILE_B + k * 4096 + wave * 1024,
+              row0 * (uint32_t)(p.sq.s * 2) + oq[k]);
+        dma16(rdo, st + ST_DO + half * TILE_B + k * 4096 + wave * 1024,
+              row0 * (uint32_t)(p.sdo.s * 2) + odo[k]);
       }
     }
-  };
-  auto store_pair = [&]() {
-#pragma unroll
-    for (int s = 0; s < 6; ++s)
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const int cidx = tid + 256 * k;
-        *reinterpret_cast<uint4*>(tiles + s * C::TILE + (cidx / CPR) * TP + (cidx % CPR) * 8) =
-            stg[s][k];
-      }
+    // (D, L) of the pair's 64 rows: 8 lanes per wave, two rows per lane.
+    if (lane < 8)
+      dma16(rdl, st + ST_DL + wave * 128,
+            (uint32_t)((t0 + 2 * it) * 32) * 8u + (uint32_t)(wave * 128 + lane * 16));
   };
 
-  // Transposed-read addressing: contraction slot (g, i) <-> tile row
-  // 8*(i/4) + 4*g + i%4 (the C-register order of S); see device_common.h.
+  // Per-lane LDS offsets within a tile.  S and dPd read row l32 (the A operand:
+  // lane = row, 8 consecutive e per lane); the transposed reads of dO^T and Q^T
+  // map contraction slot (g, i) to tile row 8*(i/4) + 4*g + i%4, the
+  // C-register order of S.
+  int aoff[NES];
+#pragma unroll
+  for (int es = 0; es < NES; ++es) aoff[es] = chunk_off<E>(l32, 2 * es + g);
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int troff[2][NEB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) troff[t][eb] = tr_off<E>(8 * t + tr_row, 32 * eb + tr_col);
   const int sk4 = (p.Sk + 3) >> 2;
 
-  if (n_it > 0) load_pair(0);
+  if (n_it > 0) issue(0);
+  if (n_it > 1) issue(1);
+#pragma unroll
+  for (int es = 0; es < NES; ++es) {  // in flight together with the first stages
+    settle(kf[es]);
+    settle(vf[es]);
+  }
+  if (n_it > 1)
+    ring_barrier<C::NPAIR_A>();
+  else
+    ring_barrier<0>();
+
   for (int it = 0; it < n_it; ++it) {
-    __syncthreads();  // previous iteration is done with the tiles
-    store_pair();
-    __syncthreads();
-    if (it + 1 < n_it) load_pair(it + 1);
+    if (it + 2 < n_it) issue(it + 2);
     const int q0 = (t0 + 2 * it + qs) * 32;
     // Skip tiles past Sq and, when causal, tiles whose rows all precede the keys.
-    if (q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs)) continue;
-    const uint16_t* tq = tiles + (3 * qs + 0) * C::TILE;
-    const uint16_t* tdo = tiles + (3 * qs + 1) * C::TILE;
-    const uint16_t* to = tiles + (3 * qs + 2) * C::TILE;
+    if (!(q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs))) {
+      const unsigned char* st = lds + (it % 3) * C::STAGE_A;
+      const unsigned char* tq = st + ST_Q + qs * TILE_B;
+      const unsigned char* tdo = st + ST_DO + qs * TILE_B;
+      const unsigned char* dl = st + ST_DL + qs * 256;
 
-    // D for row q0 + l32 (this lane's half of the columns), and LSE.
-    float dpart = 0.f;
+      f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-    for (int cc = 0; cc < CPR / 2; ++cc) {
-      const int col = (g * (CPR / 2) + cc) * 8;
-      dpart = dot8_bf16(lds_bf16x8(tdo + l32 * TP + col), lds_bf16x8(to + l32 * TP + col), dpart);
-    }
-    const float dsum = pair_sum(dpart);
-    const int qr = q0 + l32;
-    const float lse_v = (qr < p.Sq) ? lsep[qr] : 0.f;
-    if (g == 0) {
-      rv[l32] = dsum;
-      rv[32 + l32] = lse_v * kLog2e - lsc;  // exp2(S*c - this) = scale * P
-    }
-
-    f32x16 sacc = zero16(), dpacc = zero16();
-#pragma unroll
-    for (int es = 0; es < NES; ++es) {
-      sacc = mfma32x32x16(lds_bf16x8(tq + l32 * TP + es * 16 + 8 * g), kf[es], sacc);
-      dpacc = mfma32x32x16(lds_bf16x8(tdo + l32 * TP + es * 16 + 8 * g), vf[es], dpacc);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    float4 dv4[4], lv4[4];
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      dv4[cg] = *reinterpret_cast<const float4*>(rv + 8 * cg + 4 * g);
-      lv4[cg] = *reinterpret_cast<const float4*>(rv + 32 + 8 * cg + 4 * g);
-    }
-
-    // C layout: lane = key, register r = row q0 + 8*(r/4) + 4*g + r%4.
-    const bool need_mask = (CAUSAL && q0 == kbs) || (q0 + 31 >= p.Sq) || (kbs + 31 >= p.Sk);
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      const float dvals[4] = {dv4[cg].x, dv4[cg].y, dv4[cg].z, dv4[cg].w};
-      const float lvals[4] = {lv4[cg].x, lv4[cg].y, lv4[cg].z, lv4[cg].w};
-      uint32_t kbits = 0xF;
-      if (DROPOUT) kbits = keep_bits_for_key(p.drop, bh, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * cg + u;
-        float x = fmaf(sacc[r], c, -lvals[u]);
-        if (need_mask) {
-          const int qrow = q0 + 8 * cg + 4 * g + u;
-          const bool ok = (qrow < p.Sq) & (key < p.Sk) & (!CAUSAL | (key <= qrow));
-          x = ok ? x : -INFINITY;
-        }
-        const float ps = fast_exp2(x);
-        float dp = dpacc[r], pd = ps;
-        if (DROPOUT) {
-          const bool keep = (kbits >> u) & 1;
-          pd = keep ? ps * p.drop.keep_scale : 0.f;
-          dp = keep ? dp * p.drop.keep_scale : 0.f;
-        }
-        pb[r >> 3][r & 7] = (__bf16)pd;
-        dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dvals[u]));
+      for (int es = 0; es < NES; ++es) {
+        sacc = mfma32x32x16(lds_at<bf16x8>(tq, aoff[es]), kf[es], sacc);
+        dpacc = mfma32x32x16(lds_at<bf16x8>(tdo, aoff[es]), vf[es], dpacc);
       }
-    }
+      // (D, L) of rows 8*cg + 4*g + u, u = 0..3: {D0, L0, D1, L1}, {D2, L2, D3, L3}.
+      f32x4 dla[4], dlb[4];
 #pragma unroll
-    for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int off = (16 * hf + tr_row) * TP + eb * 32 + tr_col;
-        dva[eb] = mfma32x32x16(concat(lds_tr4(tdo + off), lds_tr4(tdo + off + 8 * TP)), pb[hf],
-                               dva[eb]);
-        dka[eb] = mfma32x32x16(concat(lds_tr4(tq + off), lds_tr4(tq + off + 8 * TP)), dsb[hf],
-                               dka[eb]);
+      for (int cg = 0; cg < 4; ++cg) {
+        dla[cg] = lds_at<f32x4>(dl, (8 * cg + 4 * g) * 8);
+        dlb[cg] = lds_at<f32x4>(dl, (8 * cg + 4 * g) * 8 + 16);
       }
+
+      // C layout: lane = key, register r = row q0 + 8*(r/4) + 4*g + r%4.  Only
+      // diagonal and ragged tiles take the masked variant.
+      const bool need_mask = (CAUSAL && q0 == kbs) || (q0 + 31 >= p.Sq) || (kbs + 31 >= p.Sk);
+      bf16x8 pb[2], dsb[2];
+      auto elementwise = [&](auto mask_flag) {
+        constexpr bool MASK = decltype(mask_flag)::value;
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) {
+          const float dvals[4] = {dla[cg][0], dla[cg][2], dlb[cg][0], dlb[cg][2]};
+          const float lvals[4] = {dla[cg][1], dla[cg][3], dlb[cg][1], dlb[cg][3]};
+          uint32_t kbits = 0xF;
+          if (DROPOUT)
+            kbits = keep_bits_for_key(p.drop, bh, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * cg + u;
+            float x = fmaf(sacc[r], c, -lvals[u]);
+            if (MASK) {
+              const int qrow = q0 + 8 * cg + 4 * g + u;
+              const bool ok = (qrow < p.Sq) & (key < p.Sk) & (!CAUSAL | (key <= qrow));
+              x = ok ? x : -INFINITY;
+            }
+            const float ps = fast_exp2(x);
+            float dp = dpacc[r], pd = ps;
+            if (DROPOUT) {
+              const bool keep = (kbits >> u) & 1;
+              pd = keep ? ps * p.drop.keep_scale : 0.f;
+              dp = keep ? dp * p.drop.keep_scale : 0.f;
+            }
+            pb[r >> 3][r & 7] = (__bf16)pd;
+            dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dvals[u]));
+          }
+        }
+      };
+      if (need_mask)
+        elementwise(Flag<true>{});
+      else
+        elementwise(Flag<false>{});
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
+          dva[eb] = mfma32x32x16(tr_pair(tdo, o0, o1), pb[hf], dva[eb]);
+          dka[eb] = mfma32x32x16(tr_pair(tq, o0, o1), dsb[hf], dka[eb]);
+        }
+    }
+    // Stage it+1 must have landed; stage it is free once every wave is past here.
+    if (it + 2 < n_it)
+      ring_barrier<C::NPAIR_A>();
+    else
+      ring_barrier<0>();
   }
 
   // dV = (1/scale) * sum(Pd^T dO) since Pd carries the scale; dK carries it already.
-  __syncthreads();  // the tiles are no longer read: reuse the LDS for the reduction
+  // Wave qs = 0 finalizes the first half of the columns of dV and dK, qs = 1 the rest.
   float* red = reinterpret_cast<float*>(lds);
+  const bool upper = qs == 1;
+  exchange_put<E>(dva, red, 4 * sb + 2 * qs + 0, upper, lane);
+  exchange_put<E>(dka, red, 4 * sb + 2 * qs + 1, upper, lane);
+  ring_barrier<0>();
   uint16_t* dvp = p.dv + b * p.sdv.b + h * p.sdv.h;
   uint16_t* dkp = p.dk + b * p.sdk.b + h * p.sdk.h;
-  pair_reduce_store<E>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, red, 2 * sb, qs == 1, lane);
-  pair_reduce_store<E>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, red, 2 * sb + 1, qs == 1, lane);
+  const int partner = 4 * sb + 2 * (1 - qs);
+  exchange_finish<E>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, red, partner + 0, upper, lane);
+  exchange_finish<E>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, red, partner + 1, upper, lane);
 }
 
 // ---------------------------------------------------------------------------
 template <int E, bool CAUSAL, bool DROPOUT>
 __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
   using C = BwdCfg<E>;
-  constexpr int NES = C::NES, NEB = C::NEB, TP = C::TP, CPR = C::CPR, CPT = C::CPT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
+  constexpr int ST_K = 0, ST_V = 2 * TILE_B;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int qsb = wave & 1, ks = wave >> 1;
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const int q0b = qblk * 64;
@@ -301,29 +423,26 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int qrow = q0 + l32;
   const float c = p.scale_log2;
 
-  const uint16_t* qp = p.q + b * p.sq.b + h * p.sq.h;
-  const uint16_t* dop = p.dout + b * p.sdo.b + h * p.sdo.h;
-  const uint16_t* op = p.o + b * p.so.b + h * p.so.h;
-  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(qp, p.Sq, p.sq.s, E);
-  const __amdgpu_buffer_rsrc_t rdo = rows_rsrc(dop, p.Sq, p.sdo.s, E);
-  const __amdgpu_buffer_rsrc_t ro = rows_rsrc(op, p.Sq, p.so.s, E);
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, E);
+  const __amdgpu_buffer_rsrc_t rdo =
+      rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, E);
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
   const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
 
-  // Q, dO of this row as B operands of S^T = K Q^T and dP^T = V dO^T; D and LSE of the row.
+  // Q, dO of this row as B operands of S^T = K Q^T and dP^T = V dO^T; D and L of the row.
   bf16x8 qf[NES], dof[NES];
-  float dpart = 0.f;
 #pragma unroll
   for (int es = 0; es < NES; ++es) {
     const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
     qf[es] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)qrow * (uint32_t)(p.sq.s * 2) + off16));
     dof[es] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)qrow * (uint32_t)(p.sdo.s * 2) + off16));
-    const bf16x8 o8 = __builtin_bit_cast(bf16x8, buffer_load16(ro, (uint32_t)qrow * (uint32_t)(p.so.s * 2) + off16));
-    dpart = dot8_bf16(dof[es], o8, dpart);
   }
-  const float dsum = pair_sum(dpart);
-  const float lse2 =
-      ((qrow < p.Sq) ? p.lse[(int64_t)bh * p.Sq + qrow] * kLog2e : 0.f) - __log2f(p.scale);
+  float dsum = 0.f, lse2 = 0.f;
+  if (qrow < p.Sq) {
+    const float2 dl = *reinterpret_cast<const float2*>(p.dl + ((int64_t)bh * p.Sq + qrow) * 2);
+    dsum = dl.x;
+    lse2 = dl.y;
+  }
 
   f32x16 dqa[NEB];
 #pragma unroll
@@ -332,104 +451,135 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int nkt = (p.Sk + 31) / 32;
   const int kt_end = CAUSAL ? min(nkt, min(q0b + 63, p.Sq - 1) / 32 + 1) : nkt;
   const int n_it = (kt_end + 1) / 2;
-  uint16_t* tiles = reinterpret_cast<uint16_t*>(lds);  // [key tile slot][K, V]
 
-  uint4 stg[4][CPT];
-  auto load_pair = [&](int it) {
+  // Stage it % 3 of the ring holds key tiles 2*it and 2*it + 1.
+  uint32_t okk[NLD], ov[NLD];
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) {
+    okk[k] = dma_src_offset<E>(k, tid, p.sk.s);
+    ov[k] = dma_src_offset<E>(k, tid, p.sv.s);
+  }
+  auto issue = [&](int it) {
+    unsigned char* st = lds + (it % 3) * C::STAGE_B;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int row0 = (2 * it + half) * 32;
+      const uint32_t row0 = (uint32_t)((2 * it + half) * 32);
 #pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const int cidx = tid + 256 * k;
-        const uint32_t row = (uint32_t)(row0 + cidx / CPR), col16 = (uint32_t)(cidx % CPR) * 16u;
-        stg[2 * half + 0][k] = buffer_load16(rk, row * (uint32_t)(p.sk.s * 2) + col16);
-        stg[2 * half + 1][k] = buffer_load16(rvv, row * (uint32_t)(p.sv.s * 2) + col16);
+      for (int k = 0; k < NLD; ++k) {
+        dma16(rk, st + ST_K + half * TILE_B + k * 4096 + wave * 1024,
+              row0 * (uint32_t)(p.sk.s * 2) + okk[k]);
+        dma16(rvv, st + ST_V + half * TILE_B + k * 4096 + wave * 1024,
+              row0 * (uint32_t)(p.sv.s * 2) + ov[k]);
       }
     }
   };
-  auto store_pair = [&]() {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const int cidx = tid + 256 * k;
-        *reinterpret_cast<uint4*>(tiles + s * C::TILE + (cidx / CPR) * TP + (cidx % CPR) * 8) =
-            stg[s][k];
-      }
-  };
 
+  int aoff[NES];
+#pragma unroll
+  for (int es = 0; es < NES; ++es) aoff[es] = chunk_off<E>(l32, 2 * es + g);
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int troff[2][NEB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb) troff[t][eb] = tr_off<E>(8 * t + tr_row, 32 * eb + tr_col);
   const int key_limit = CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1;
   const int sk4 = (p.Sk + 3) >> 2;
   uint64_t drow = 0;
   if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
 
-  if (n_it > 0) load_pair(0);
+  if (n_it > 0) issue(0);
+  if (n_it > 1) issue(1);
+#pragma unroll
+  for (int es = 0; es < NES; ++es) {  // in flight together with the first stages
+    settle(qf[es]);
+    settle(dof[es]);
+  }
+  if (n_it > 1)
+    ring_barrier<C::NPAIR_B>();
+  else
+    ring_barrier<0>();
+
   for (int it = 0; it < n_it; ++it) {
-    __syncthreads();
-    store_pair();
-    __syncthreads();
-    if (it + 1 < n_it) load_pair(it + 1);
+    if (it + 2 < n_it) issue(it + 2);
     const int j = 2 * it + ks;
     const int k0 = j * 32;
-    if (j >= kt_end || (CAUSAL && k0 > q0 + 31)) continue;
-    const uint16_t* tk = tiles + (2 * ks + 0) * C::TILE;
-    const uint16_t* tv = tiles + (2 * ks + 1) * C::TILE;
+    if (!(j >= kt_end || (CAUSAL && k0 > q0 + 31))) {
+      const unsigned char* st = lds + (it % 3) * C::STAGE_B;
+      const unsigned char* tk = st + ST_K + ks * TILE_B;
+      const unsigned char* tv = st + ST_V + ks * TILE_B;
 
-    // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
-    f32x16 sacc = zero16(), dpacc = zero16();
+      // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
+      f32x16 sacc = zero16(), dpacc = zero16();
 #pragma unroll
-    for (int es = 0; es < NES; ++es) {
-      sacc = mfma32x32x16(lds_bf16x8(tk + l32 * TP + es * 16 + 8 * g), qf[es], sacc);
-      dpacc = mfma32x32x16(lds_bf16x8(tv + l32 * TP + es * 16 + 8 * g), dof[es], dpacc);
-    }
+      for (int es = 0; es < NES; ++es) {
+        sacc = mfma32x32x16(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
+        dpacc = mfma32x32x16(lds_at<bf16x8>(tv, aoff[es]), dof[es], dpacc);
+      }
 
-    const bool need_mask = (k0 + 31 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1));
-    const int lim = key_limit - k0 - 4 * g;
-    bf16x8 dsb[2];
+      // Only tiles that reach the diagonal or past Sk take the masked variant.
+      const bool need_mask = (k0 + 31 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1));
+      const int lim = key_limit - k0 - 4 * g;
+      bf16x8 dsb[2];
+      auto elementwise = [&](auto mask_flag) {
+        constexpr bool MASK = decltype(mask_flag)::value;
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) {
-      uint32_t kbits = 0xF;
-      if (DROPOUT) {
-        const PhiloxOut w = philox4x32_10(drow + (uint32_t)(k0 >> 2) + 2 * cg + g, p.drop.seed_lo,
-                                          p.drop.seed_hi);
-        kbits = (w.w[0] >= p.drop.threshold ? 1u : 0u) | (w.w[1] >= p.drop.threshold ? 2u : 0u) |
-                (w.w[2] >= p.drop.threshold ? 4u : 0u) | (w.w[3] >= p.drop.threshold ? 8u : 0u);
-      }
+        for (int cg = 0; cg < 4; ++cg) {
+          uint32_t kbits = 0xF;
+          if (DROPOUT) {
+            const PhiloxOut w = philox4x32_10(drow + (uint32_t)(k0 >> 2) + 2 * cg + g,
+                                              p.drop.seed_lo, p.drop.seed_hi);
+            kbits = (w.w[0] >= p.drop.threshold ? 1u : 0u) |
+                    (w.w[1] >= p.drop.threshold ? 2u : 0u) |
+                    (w.w[2] >= p.drop.threshold ? 4u : 0u) |
+                    (w.w[3] >= p.drop.threshold ? 8u : 0u);
+          }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * cg + u;
-        float x = fmaf(sacc[r], c, -lse2);
-        if (need_mask) x = (8 * cg + u <= lim) ? x : -INFINITY;
-        const float ps = fast_exp2(x);
-        float dp = dpacc[r];
-        if (DROPOUT) dp = ((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f;
-        dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dsum));
-      }
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * cg + u;
+            float x = fmaf(sacc[r], c, -lse2);
+            if (MASK) x = (8 * cg + u <= lim) ? x : -INFINITY;
+            const float ps = fast_exp2(x);
+            float dp = dpacc[r];
+            if (DROPOUT) dp = ((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f;
+            dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dsum));
+          }
+        }
+      };
+      if (need_mask)
+        elementwise(Flag<true>{});
+      else
+        elementwise(Flag<false>{});
+      // dQ^T += K^T dS'^T: A = K^T read transposed from the tile, B = dS'^T from registers.
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
+          dqa[eb] = mfma32x32x16(tr_pair(tk, o0, o1), dsb[hf], dqa[eb]);
+        }
     }
-    // dQ^T += K^T dS'^T: A = K^T read transposed from the tile, B = dS'^T from registers.
-#pragma unroll
-    for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint16_t* ak = tk + (16 * hf + tr_row) * TP + eb * 32 + tr_col;
-        dqa[eb] = mfma32x32x16(concat(lds_tr4(ak), lds_tr4(ak + 8 * TP)), dsb[hf], dqa[eb]);
-      }
+    if (it + 2 < n_it)
+      ring_barrier<C::NPAIR_B>();
+    else
+      ring_barrier<0>();
   }
 
-  __syncthreads();
+  // Wave ks = 0 finalizes the first half of dQ's columns, ks = 1 the rest.
   float* red = reinterpret_cast<float*>(lds);
+  const bool upper = ks == 1;
+  exchange_put<E>(dqa, red, 2 * qsb + ks, upper, lane);
+  ring_barrier<0>();
   uint16_t* dqp = p.dq + b * p.sdq.b + h * p.sdq.h;
-  pair_reduce_store<E>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, red, qsb, ks == 1, lane);
+  exchange_finish<E>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, red, 2 * qsb + (1 - ks), upper, lane);
 }
 
 // Workgroup order: per head, dK/dV and dQ blocks alternate, heaviest causal
 // blocks first; all blocks of a head sit on one XCD when the head count allows.
 template <int E, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E>::TOTAL];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E>::LDS_B];
   const int bh_count = p.B * p.H;
   int bh, slot;
   if ((bh_count & 7) == 0) {
@@ -457,8 +607,39 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb)
     role_dq<E, CAUSAL, DROPOUT>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
+// D_i = rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every row.
+// CPR lanes share a row; each loads one 16-byte chunk of dO and of O.
+template <int E>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int CPR = E / 8, RPB = 256 / CPR;
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / CPR;
+  const int col = tid % CPR;
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  float d = 0.f;
+  if (row < rows) {
+    const int64_t bh = row / p.Sq;
+    const int64_t i = row - bh * p.Sq;
+    const int64_t b = bh / p.H, h = bh - (bh / p.H) * p.H;
+    const bf16x8 x = load_bf16x8(p.dout + b * p.sdo.b + h * p.sdo.h + i * p.sdo.s + col * 8);
+    const bf16x8 y = load_bf16x8(p.o + b * p.so.b + h * p.so.h + i * p.so.s + col * 8);
+    d = dot8_bf16(x, y, 0.f);
+  }
+  d = group_sum<CPR>(d);
+  if (row < rows && col == 0) {
+    float2 out;
+    out.x = d;
+    out.y = p.lse[row] * kLog2e - __log2f(p.scale);
+    *reinterpret_cast<float2*>(p.dl + row * 2) = out;
+  }
+}
+
 template <int E>
 hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
+  constexpr int RPB = 256 / (E / 8);
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  hipLaunchKernelGGL((bwd_prep_kernel<E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, p);
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
   if (causal) {
@@ -476,6 +657,11 @@ hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream
 }
 
 }  // namespace
+
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
+  const size_t raw = (size_t)B * (size_t)H * (size_t)Sq * 8u;
+  return (raw + 255u) & ~(size_t)255u;
+}
 
 hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream) {
   return E == 64 ? launch_bwd_t<64>(p, causal, dropout, stream)

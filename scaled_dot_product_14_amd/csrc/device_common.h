@@ -116,4 +116,34 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   return __builtin_bit_cast(uint2, v);
 }
 
+// Within-row lane permutations (DPP): xor 1, xor 2 (quad_perm), and the
+// mirrors of each 8-lane half row and of the 16-lane row.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of N lanes (N = 8 or 16), result in every lane of the group.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x += dpp_move<kDppXor1>(x);
+  x += dpp_move<kDppXor2>(x);
+  x += dpp_move<kDppHalfMirror>(x);
+  if (N == 16) x += dpp_move<kDppMirror>(x);
+  return x;
+}
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
+// Waits here for the load that produced x.  A register loaded before a loop
+// and first read inside it otherwise stays "in flight" at the loop header in
+// the compiler's wait bookkeeping, and every iteration then waits for all
+// loads issued before that read, prefetches included.
+__device__ __forceinline__ void settle(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+
 }  // namespace sdpa14

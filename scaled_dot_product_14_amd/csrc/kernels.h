@@ -36,6 +36,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   const float* lse;  // contiguous [B, H, Sq]
+  float* dl;         // workspace: (D_i, LSE_i*log2(e) - log2(scale)) per row, [B, H, Sq, 2]
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Sq, Sk;
   float scale;       // softmax scale
@@ -57,7 +58,10 @@ struct TileChoice {
 
 hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
                       const TileChoice& tiles, hipStream_t stream);
+// Backward: a row pass filling p.dl, then the main kernel.  p.dl must hold
+// bwd_workspace_bytes(B, H, Sq) bytes.
 hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream);
+size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream);
 
 }  // namespace sdpa14

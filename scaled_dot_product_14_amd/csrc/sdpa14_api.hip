@@ -90,8 +90,10 @@ bool same_shape(const Desc& a, const Desc& b) {
 }
 
 // Kernels read rows of one (batch, head) slice through 32-bit buffer offsets.
+// Kernels address a (batch, head) slice with 32-bit byte offsets, including the
+// rows of a tile that run past S (up to 127 of them; those read as zeros).
 bool slice_ok(const Desc& t) {
-  return (t.S - 1) * t.st.s * 2 + t.E * 2 < (int64_t(1) << 31);
+  return (t.S + 127) * t.st.s * 2 + t.E * 2 < (int64_t(1) << 31);
 }
 
 int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
@@ -249,7 +251,8 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
 int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
              const sdpa_tensor* v, const sdpa_tensor* out, const float* lse, double dropout_p,
              int is_causal, uint64_t seed, uint64_t offset, double scale, const sdpa_tensor* dq,
-             const sdpa_tensor* dk, const sdpa_tensor* dv, sdpa_stream_t stream) {
+             const sdpa_tensor* dk, const sdpa_tensor* dv, void* workspace,
+             size_t workspace_bytes, sdpa_stream_t stream) {
   Desc ddo, dqi, dki, dvi, dout_i, dqo, dko, dvo;
   int rc;
   if ((rc = check_tensor(dout, "dout", &ddo))) return rc;
@@ -274,6 +277,11 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   if ((rc = check_dropout(dropout_p))) return rc;
   float sc;
   if ((rc = resolve_scale(scale, dqi.E, &sc))) return rc;
+  if (workspace == nullptr) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < bwd_workspace_bytes(dqi.B, dqi.H, dqi.S))
+    return fail(SDPA_ERR_WORKSPACE, "workspace is smaller than sdpa_bwd_workspace_size()");
 
   BwdParams p;
   p.q = dqi.ptr;
@@ -285,6 +293,7 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   p.dk = const_cast<uint16_t*>(dko.ptr);
   p.dv = const_cast<uint16_t*>(dvo.ptr);
   p.lse = lse;
+  p.dl = static_cast<float*>(workspace);
   p.sq = dqi.st;
   p.sk = dki.st;
   p.sv = dvi.st;
@@ -307,6 +316,11 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
                                       [&] { return launch_bwd(p, E, causal, drop, st); });
   return hip_status(err, "backward launch");
+}
+
+size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq) {
+  if (B <= 0 || H <= 0 || Sq <= 0) return 0;
+  return bwd_workspace_bytes(B, H, Sq);
 }
 
 void sdpa_set_rng_state(uint64_t seed, uint64_t offset) {

@@ -96,12 +96,16 @@ def test_forward_rejects_bad_arguments(lib, kw, code, needle):
     assert bnd.sdpa_get_rng_state() == (1234, 99)
 
 
+WS_BYTES = 1 << 20  # ample for the default shapes (B*H*Sq*8 = 2 KiB)
+
+
 def _bwd(lib, **over):
     t = {n: over.get(n) or _t() for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
     return lib.sdpa_bwd(*(ctypes.byref(t[n]) for n in ("dout", "q", "k", "v", "out")),
                         over.get("lse", FAKE), over.get("p", 0.0), 1, 0, 0,
                         over.get("scale", math.nan),
-                        *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")), None)
+                        *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")),
+                        over.get("ws", FAKE), over.get("ws_bytes", WS_BYTES), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -119,6 +123,28 @@ def test_backward_rejects_bad_arguments(lib, kw, code):
     rc = _bwd(lib, **kw)
     assert rc == code, (rc, _err(lib))
     assert bnd.sdpa_get_rng_state() == (5, 6)
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(ws=0), "NULL"),
+    (dict(ws=FAKE + 128), "aligned"),
+    (dict(ws_bytes=2047), "smaller"),
+])
+def test_backward_checks_workspace(lib, kw, needle):
+    bnd.sdpa_set_rng_state(7, 8)
+    rc = _bwd(lib, **kw)
+    assert rc == bnd.SDPA_ERR_WORKSPACE, (rc, _err(lib))
+    assert needle.lower() in _err(lib).lower()
+    assert bnd.sdpa_get_rng_state() == (7, 8)
+
+
+def test_workspace_size():
+    # 8 bytes per query row (D and the base-2 LSE), rounded up to 256 bytes.
+    assert sdpa.sdpa_bwd_workspace_size(1, 2, 128) == 2048
+    assert sdpa.sdpa_bwd_workspace_size(1, 1, 1) == 256
+    assert sdpa.sdpa_bwd_workspace_size(2, 12, 1024) == 2 * 12 * 1024 * 8
+    assert sdpa.sdpa_bwd_workspace_size(3, 5, 77) == (3 * 5 * 77 * 8 + 255) // 256 * 256
+    assert sdpa.sdpa_bwd_workspace_size(0, 1, 1) == 0
 
 
 def test_slice_too_large_is_unsupported(lib):
