@@ -62,6 +62,7 @@ struct BwdCfg {
   static constexpr int ROW_B = 2 * E;
   static constexpr int TILE_B = 32 * ROW_B;
   static constexpr int NLD = TILE_B / (256 * 16);  // LDS-DMA loads per thread per tile
+  static_assert(NLD == E / 64, "tile loads");
   static constexpr int DL_B = 64 * 8;              // (D, L) of the pair's 64 rows
   static constexpr int STAGE_A = 4 * TILE_B + DL_B;  // Q, Q', dO, dO', (D, L)
   static constexpr int STAGE_B = 4 * TILE_B;         // K, K', V, V'
@@ -70,7 +71,8 @@ struct BwdCfg {
   static constexpr int NPAIR_B = 4 * NLD;      // loads per thread per stage, dQ role
   static constexpr int RED_B = 4 * NEB * 16 * 64 * 4;  // end-of-block exchange
   static constexpr int LDS_B = NSTAGE * STAGE_A;
-  static_assert(STAGE_A >= STAGE_B && LDS_B >= RED_B, "LDS budget");
+  // The dQ role's stage 2 also takes the block's (D, L) in the prologue.
+  static_assert(STAGE_A >= STAGE_B + DL_B && LDS_B >= RED_B, "LDS budget");
 };
 
 // s_waitcnt with vmcnt <= VM and lgkmcnt == 0 (gfx9 encoding: vmcnt in bits
@@ -98,13 +100,14 @@ __device__ __forceinline__ void ring_barrier() {
 // from inline assembly so that the compiler's wait bookkeeping does not tie
 // later LDS reads of other stages to these loads; the ring barrier waits for
 // them explicitly.  M0 carries the LDS address (the compiler sets M0 afresh
-// before each of its own uses).
+// before each of its own uses); an LDS-DMA instruction needs one wait state
+// after the SALU write of M0.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is a reserved register
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_wave,
                                       uint32_t voff) {
   const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(dst), "v"(voff), "s"(r)
                : "m0");
@@ -125,6 +128,27 @@ __device__ __forceinline__ uint32_t dma_src_offset(int k, int tid, int64_t row_s
   const int slot = k * 256 + tid;
   const int row = slot / CPR, pos = slot % CPR;
   return (uint32_t)row * (uint32_t)(row_stride * 2) + (uint32_t)((pos ^ tile_swz<E>(row)) * 16);
+}
+
+// Loads rows row0 .. row0+63 of x and of y, two 32-row tiles each, into a
+// stage laid out [x rows 0-31][x rows 32-63][y rows 0-31][y rows 32-63].  ox,
+// oy are the thread's dma_src_offset values; x_row, y_row the row strides in bytes.
+template <int E>
+__device__ __forceinline__ void issue_tiles(unsigned char* st, int wave, uint32_t row0,
+                                            __amdgpu_buffer_rsrc_t rx, uint32_t x_row,
+                                            const uint32_t (&ox)[E / 64],
+                                            __amdgpu_buffer_rsrc_t ry, uint32_t y_row,
+                                            const uint32_t (&oy)[E / 64]) {
+  constexpr int TILE_B = 64 * E, NLD = E / 64;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t r = row0 + 32u * half;
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      dma16(rx, st + half * TILE_B + k * 4096 + wave * 1024, r * x_row + ox[k]);
+      dma16(ry, st + (2 + half) * TILE_B + k * 4096 + wave * 1024, r * y_row + oy[k]);
+    }
+  }
 }
 
 // LDS byte offset, within a tile, of the chunk holding elements 8c .. 8c+7 of row r.
@@ -242,15 +266,6 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
   const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
 
-  // K, V of the sub-block as B operands of S = Q K^T and dPd = dO V^T: lane = key,
-  // e = 16*es + 8*g + 0..7.  Keys past Sk read as zeros.
-  bf16x8 kf[NES], vf[NES];
-#pragma unroll
-  for (int es = 0; es < NES; ++es) {
-    const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
-    kf[es] = __builtin_bit_cast(bf16x8, buffer_load16(rk, (uint32_t)key * (uint32_t)(p.sk.s * 2) + off16));
-    vf[es] = __builtin_bit_cast(bf16x8, buffer_load16(rvv, (uint32_t)key * (uint32_t)(p.sv.s * 2) + off16));
-  }
   f32x16 dva[NEB], dka[NEB];
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) {
@@ -271,17 +286,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   }
   auto issue = [&](int it) {
     unsigned char* st = lds + (it % 3) * C::STAGE_A;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t row0 = (uint32_t)((t0 + 2 * it + half) * 32);
-#pragma unroll
-      for (int k = 0; k < NLD; ++k) {
-        dma16(rq, st + ST_Q + half * TILE_B + k * 4096 + wave * 1024,
-              row0 * (uint32_t)(p.sq.s * 2) + oq[k]);
-        dma16(rdo, st + ST_DO + half * TILE_B + k * 4096 + wave * 1024,
-              row0 * (uint32_t)(p.sdo.s * 2) + odo[k]);
-      }
-    }
+    issue_tiles<E>(st + ST_Q, wave, (uint32_t)((t0 + 2 * it) * 32), rq, (uint32_t)(p.sq.s * 2),
+                   oq, rdo, (uint32_t)(p.sdo.s * 2), odo);
     // (D, L) of the pair's 64 rows: 8 lanes per wave, two rows per lane.
     if (lane < 8)
       dma16(rdl, st + ST_DL + wave * 128,
@@ -304,12 +310,33 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     for (int eb = 0; eb < NEB; ++eb) troff[t][eb] = tr_off<E>(8 * t + tr_row, 32 * eb + tr_col);
   const int sk4 = (p.Sk + 3) >> 2;
 
+  // K and V of the block pass through stage 2 (first refilled by iteration 0)
+  // together with the first two stages; each wave then takes its sub-block's
+  // fragments, the B operands of S = Q K^T and dPd = dO V^T: lane = key,
+  // e = 16*es + 8*g + 0..7 (keys past Sk read as zeros).
+  {
+    uint32_t okv[NLD], ovv[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      okv[k] = dma_src_offset<E>(k, tid, p.sk.s);
+      ovv[k] = dma_src_offset<E>(k, tid, p.sv.s);
+    }
+    issue_tiles<E>(lds + 2 * C::STAGE_A, wave, (uint32_t)kb0, rk, (uint32_t)(p.sk.s * 2), okv, rvv,
+                   (uint32_t)(p.sv.s * 2), ovv);
+  }
   if (n_it > 0) issue(0);
   if (n_it > 1) issue(1);
+  if (n_it > 1)
+    ring_barrier<2 * C::NPAIR_A>();
+  else if (n_it > 0)
+    ring_barrier<C::NPAIR_A>();
+  else
+    ring_barrier<0>();
+  bf16x8 kf[NES], vf[NES];
 #pragma unroll
-  for (int es = 0; es < NES; ++es) {  // in flight together with the first stages
-    settle(kf[es]);
-    settle(vf[es]);
+  for (int es = 0; es < NES; ++es) {
+    kf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_A + sb * TILE_B, aoff[es]);
+    vf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_A + (2 + sb) * TILE_B, aoff[es]);
   }
   if (n_it > 1)
     ring_barrier<C::NPAIR_A>();
@@ -317,10 +344,13 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     ring_barrier<0>();
 
   for (int it = 0; it < n_it; ++it) {
-    if (it + 2 < n_it) issue(it + 2);
     const int q0 = (t0 + 2 * it + qs) * 32;
     // Skip tiles past Sq and, when causal, tiles whose rows all precede the keys.
-    if (!(q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs))) {
+    const bool active = !(q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs));
+    // The next loads are issued after the first products, so that a wave held
+    // up issuing them still has matrix work in flight.
+    if (!active && it + 2 < n_it) issue(it + 2);
+    if (active) {
       const unsigned char* st = lds + (it % 3) * C::STAGE_A;
       const unsigned char* tq = st + ST_Q + qs * TILE_B;
       const unsigned char* tdo = st + ST_DO + qs * TILE_B;
@@ -332,6 +362,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
         sacc = mfma32x32x16(lds_at<bf16x8>(tq, aoff[es]), kf[es], sacc);
         dpacc = mfma32x32x16(lds_at<bf16x8>(tdo, aoff[es]), vf[es], dpacc);
       }
+      if (it + 2 < n_it) issue(it + 2);
       // (D, L) of rows 8*cg + 4*g + u, u = 0..3: {D0, L0, D1, L1}, {D2, L2, D3, L3}.
       f32x4 dla[4], dlb[4];
 #pragma unroll
@@ -429,20 +460,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
   const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
 
-  // Q, dO of this row as B operands of S^T = K Q^T and dP^T = V dO^T; D and L of the row.
-  bf16x8 qf[NES], dof[NES];
-#pragma unroll
-  for (int es = 0; es < NES; ++es) {
-    const uint32_t off16 = (uint32_t)(es * 16 + 8 * g) * 2u;
-    qf[es] = __builtin_bit_cast(bf16x8, buffer_load16(rq, (uint32_t)qrow * (uint32_t)(p.sq.s * 2) + off16));
-    dof[es] = __builtin_bit_cast(bf16x8, buffer_load16(rdo, (uint32_t)qrow * (uint32_t)(p.sdo.s * 2) + off16));
-  }
-  float dsum = 0.f, lse2 = 0.f;
-  if (qrow < p.Sq) {
-    const float2 dl = *reinterpret_cast<const float2*>(p.dl + ((int64_t)bh * p.Sq + qrow) * 2);
-    dsum = dl.x;
-    lse2 = dl.y;
-  }
+  const __amdgpu_buffer_rsrc_t rdl = make_rsrc(p.dl + (int64_t)bh * p.Sq * 2, (uint32_t)p.Sq * 8u);
 
   f32x16 dqa[NEB];
 #pragma unroll
@@ -460,18 +478,8 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     ov[k] = dma_src_offset<E>(k, tid, p.sv.s);
   }
   auto issue = [&](int it) {
-    unsigned char* st = lds + (it % 3) * C::STAGE_B;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t row0 = (uint32_t)((2 * it + half) * 32);
-#pragma unroll
-      for (int k = 0; k < NLD; ++k) {
-        dma16(rk, st + ST_K + half * TILE_B + k * 4096 + wave * 1024,
-              row0 * (uint32_t)(p.sk.s * 2) + okk[k]);
-        dma16(rvv, st + ST_V + half * TILE_B + k * 4096 + wave * 1024,
-              row0 * (uint32_t)(p.sv.s * 2) + ov[k]);
-      }
-    }
+    issue_tiles<E>(lds + (it % 3) * C::STAGE_B + ST_K, wave, (uint32_t)(64 * it), rk,
+                   (uint32_t)(p.sk.s * 2), okk, rvv, (uint32_t)(p.sv.s * 2), ov);
   };
 
   int aoff[NES];
@@ -489,23 +497,50 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   uint64_t drow = 0;
   if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
 
+  // Q and dO of the block pass through stage 2 (first refilled by iteration 0)
+  // together with the first two stages; each wave then takes its rows'
+  // fragments, the B operands of S^T = K Q^T and dP^T = V dO^T.
+  {
+    uint32_t oqq[NLD], odd[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      oqq[k] = dma_src_offset<E>(k, tid, p.sq.s);
+      odd[k] = dma_src_offset<E>(k, tid, p.sdo.s);
+    }
+    issue_tiles<E>(lds + 2 * C::STAGE_B, wave, (uint32_t)q0b, rq, (uint32_t)(p.sq.s * 2), oqq, rdo,
+                   (uint32_t)(p.sdo.s * 2), odd);
+    // (D, L) of the block's 64 rows: 8 lanes per wave, two rows per lane.
+    if (lane < 8)
+      dma16(rdl, lds + 2 * C::STAGE_B + 4 * TILE_B + wave * 128,
+            (uint32_t)q0b * 8u + (uint32_t)(wave * 128 + lane * 16));
+  }
   if (n_it > 0) issue(0);
   if (n_it > 1) issue(1);
+  if (n_it > 1)
+    ring_barrier<2 * C::NPAIR_B>();
+  else if (n_it > 0)
+    ring_barrier<C::NPAIR_B>();
+  else
+    ring_barrier<0>();
+  bf16x8 qf[NES], dof[NES];
 #pragma unroll
-  for (int es = 0; es < NES; ++es) {  // in flight together with the first stages
-    settle(qf[es]);
-    settle(dof[es]);
+  for (int es = 0; es < NES; ++es) {
+    qf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_B + qsb * TILE_B, aoff[es]);
+    dof[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_B + (2 + qsb) * TILE_B, aoff[es]);
   }
+  const float2 dl_row = lds_at<float2>(lds + 2 * C::STAGE_B + 4 * TILE_B, (qsb * 32 + l32) * 8);
+  const float dsum = dl_row.x, lse2 = dl_row.y;  // D and L of the row
   if (n_it > 1)
     ring_barrier<C::NPAIR_B>();
   else
     ring_barrier<0>();
 
   for (int it = 0; it < n_it; ++it) {
-    if (it + 2 < n_it) issue(it + 2);
     const int j = 2 * it + ks;
     const int k0 = j * 32;
-    if (!(j >= kt_end || (CAUSAL && k0 > q0 + 31))) {
+    const bool active = !(j >= kt_end || (CAUSAL && k0 > q0 + 31));
+    if (!active && it + 2 < n_it) issue(it + 2);
+    if (active) {
       const unsigned char* st = lds + (it % 3) * C::STAGE_B;
       const unsigned char* tk = st + ST_K + ks * TILE_B;
       const unsigned char* tv = st + ST_V + ks * TILE_B;
@@ -517,6 +552,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
         sacc = mfma32x32x16(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
         dpacc = mfma32x32x16(lds_at<bf16x8>(tv, aoff[es]), dof[es], dpacc);
       }
+      if (it + 2 < n_it) issue(it + 2);
 
       // Only tiles that reach the diagonal or past Sk take the masked variant.
       const bool need_mask = (k0 + 31 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1));
