@@ -63,8 +63,8 @@ struct BwdCfg {
   static constexpr int TILE_B = 32 * ROW_B;
   static constexpr int NLD = TILE_B / (256 * 16);  // LDS-DMA loads per thread per tile
   static_assert(NLD == E / 64, "tile loads");
-  static constexpr int DL_B = 64 * 8;              // (D, L) of the pair's 64 rows
-  static constexpr int STAGE_A = 4 * TILE_B + DL_B;  // Q, Q', dO, dO', (D, L)
+  static constexpr int DL_B = 64 * 8;              // -D and L of the pair's 64 rows
+  static constexpr int STAGE_A = 4 * TILE_B + DL_B;  // Q, Q', dO, dO', -D, L
   static constexpr int STAGE_B = 4 * TILE_B;         // K, K', V, V'
   static constexpr int NSTAGE = 3;
   static constexpr int NPAIR_A = 4 * NLD + 1;  // loads per thread per stage, dK/dV role
@@ -162,6 +162,13 @@ __device__ __forceinline__ int chunk_off(int r, int c) {
 template <int E>
 __device__ __forceinline__ int tr_off(int r, int e) {
   return r * (2 * E) + (((e >> 3) ^ tile_swz<E>(r)) << 4) + ((e & 4) << 1);
+}
+
+// Byte offset of ring stage it % 3 as one wave-uniform scalar, so that LDS
+// addresses are a per-lane base plus this offset plus an immediate.
+template <int STAGE>
+__device__ __forceinline__ uint32_t ring_offset(int it) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((it % 3) * STAGE);
 }
 
 template <typename T>
@@ -262,7 +269,9 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, E);
   const __amdgpu_buffer_rsrc_t rdo =
       rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, E);
-  const __amdgpu_buffer_rsrc_t rdl = make_rsrc(p.dl + (int64_t)bh * p.Sq * 2, (uint32_t)p.Sq * 8u);
+  // Waves 0, 1 stage rows of -D, waves 2, 3 rows of L (workspace planes).
+  const __amdgpu_buffer_rsrc_t rdl = make_rsrc(
+      p.dl + (wave >> 1) * ((int64_t)p.B * p.H * p.Sq) + (int64_t)bh * p.Sq, (uint32_t)p.Sq * 4u);
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
   const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
 
@@ -285,13 +294,13 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     odo[k] = dma_src_offset<E>(k, tid, p.sdo.s);
   }
   auto issue = [&](int it) {
-    unsigned char* st = lds + (it % 3) * C::STAGE_A;
+    unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
     issue_tiles<E>(st + ST_Q, wave, (uint32_t)((t0 + 2 * it) * 32), rq, (uint32_t)(p.sq.s * 2),
                    oq, rdo, (uint32_t)(p.sdo.s * 2), odo);
-    // (D, L) of the pair's 64 rows: 8 lanes per wave, two rows per lane.
+    // -D (waves 0, 1) and L (waves 2, 3) of the pair's 64 rows, 4 rows per lane.
     if (lane < 8)
       dma16(rdl, st + ST_DL + wave * 128,
-            (uint32_t)((t0 + 2 * it) * 32) * 8u + (uint32_t)(wave * 128 + lane * 16));
+            (uint32_t)((t0 + 2 * it) * 32) * 4u + (uint32_t)((wave & 1) * 128 + lane * 16));
   };
 
   // Per-lane LDS offsets within a tile.  S and dPd read row l32 (the A operand:
@@ -351,25 +360,28 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     // up issuing them still has matrix work in flight.
     if (!active && it + 2 < n_it) issue(it + 2);
     if (active) {
-      const unsigned char* st = lds + (it % 3) * C::STAGE_A;
+      const unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
       const unsigned char* tq = st + ST_Q + qs * TILE_B;
       const unsigned char* tdo = st + ST_DO + qs * TILE_B;
-      const unsigned char* dl = st + ST_DL + qs * 256;
+      const unsigned char* dl = st + ST_DL + qs * 128;
 
-      f32x16 sacc = zero16(), dpacc = zero16();
+      // -D and L of rows 8*cg + 4*g + u sit in register order: -D seeds dPd's
+      // accumulator, so the products yield dPd - D directly (without dropout).
+      f32x4 nd4[4], l4[4];
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        nd4[cg] = lds_at<f32x4>(dl, (8 * cg + 4 * g) * 4);
+        l4[cg] = lds_at<f32x4>(dl, 256 + (8 * cg + 4 * g) * 4);
+      }
+      f32x16 sacc = zero16(), dpacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dpacc[r] = DROPOUT ? 0.f : nd4[r >> 2][r & 3];
 #pragma unroll
       for (int es = 0; es < NES; ++es) {
         sacc = mfma32x32x16(lds_at<bf16x8>(tq, aoff[es]), kf[es], sacc);
         dpacc = mfma32x32x16(lds_at<bf16x8>(tdo, aoff[es]), vf[es], dpacc);
       }
       if (it + 2 < n_it) issue(it + 2);
-      // (D, L) of rows 8*cg + 4*g + u, u = 0..3: {D0, L0, D1, L1}, {D2, L2, D3, L3}.
-      f32x4 dla[4], dlb[4];
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        dla[cg] = lds_at<f32x4>(dl, (8 * cg + 4 * g) * 8);
-        dlb[cg] = lds_at<f32x4>(dl, (8 * cg + 4 * g) * 8 + 16);
-      }
 
       // C layout: lane = key, register r = row q0 + 8*(r/4) + 4*g + r%4.  Only
       // diagonal and ragged tiles take the masked variant.
@@ -379,29 +391,27 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
         constexpr bool MASK = decltype(mask_flag)::value;
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
-          const float dvals[4] = {dla[cg][0], dla[cg][2], dlb[cg][0], dlb[cg][2]};
-          const float lvals[4] = {dla[cg][1], dla[cg][3], dlb[cg][1], dlb[cg][3]};
           uint32_t kbits = 0xF;
           if (DROPOUT)
             kbits = keep_bits_for_key(p.drop, bh, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * cg + u;
-            float x = fmaf(sacc[r], c, -lvals[u]);
+            float x = fmaf(sacc[r], c, -l4[cg][u]);
             if (MASK) {
               const int qrow = q0 + 8 * cg + 4 * g + u;
               const bool ok = (qrow < p.Sq) & (key < p.Sk) & (!CAUSAL | (key <= qrow));
               x = ok ? x : -INFINITY;
             }
             const float ps = fast_exp2(x);
-            float dp = dpacc[r], pd = ps;
+            float dp = dpacc[r], pd = ps;  // dp = dPd - D without dropout
             if (DROPOUT) {
               const bool keep = (kbits >> u) & 1;
               pd = keep ? ps * p.drop.keep_scale : 0.f;
-              dp = keep ? dp * p.drop.keep_scale : 0.f;
+              dp = (keep ? dp * p.drop.keep_scale : 0.f) + nd4[cg][u];
             }
             pb[r >> 3][r & 7] = (__bf16)pd;
-            dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dvals[u]));
+            dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
           }
         }
       };
@@ -460,7 +470,9 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
   const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
 
-  const __amdgpu_buffer_rsrc_t rdl = make_rsrc(p.dl + (int64_t)bh * p.Sq * 2, (uint32_t)p.Sq * 8u);
+  // Waves 0, 1 stage rows of -D, waves 2, 3 rows of L (workspace planes).
+  const __amdgpu_buffer_rsrc_t rdl = make_rsrc(
+      p.dl + (wave >> 1) * ((int64_t)p.B * p.H * p.Sq) + (int64_t)bh * p.Sq, (uint32_t)p.Sq * 4u);
 
   f32x16 dqa[NEB];
 #pragma unroll
@@ -478,7 +490,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     ov[k] = dma_src_offset<E>(k, tid, p.sv.s);
   }
   auto issue = [&](int it) {
-    issue_tiles<E>(lds + (it % 3) * C::STAGE_B + ST_K, wave, (uint32_t)(64 * it), rk,
+    issue_tiles<E>(lds + ring_offset<C::STAGE_B>(it) + ST_K, wave, (uint32_t)(64 * it), rk,
                    (uint32_t)(p.sk.s * 2), okk, rvv, (uint32_t)(p.sv.s * 2), ov);
   };
 
@@ -509,10 +521,10 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     }
     issue_tiles<E>(lds + 2 * C::STAGE_B, wave, (uint32_t)q0b, rq, (uint32_t)(p.sq.s * 2), oqq, rdo,
                    (uint32_t)(p.sdo.s * 2), odd);
-    // (D, L) of the block's 64 rows: 8 lanes per wave, two rows per lane.
+    // -D (waves 0, 1) and L (waves 2, 3) of the block's 64 rows, 4 rows per lane.
     if (lane < 8)
       dma16(rdl, lds + 2 * C::STAGE_B + 4 * TILE_B + wave * 128,
-            (uint32_t)q0b * 8u + (uint32_t)(wave * 128 + lane * 16));
+            (uint32_t)q0b * 4u + (uint32_t)((wave & 1) * 128 + lane * 16));
   }
   if (n_it > 0) issue(0);
   if (n_it > 1) issue(1);
@@ -528,8 +540,12 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     qf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_B + qsb * TILE_B, aoff[es]);
     dof[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_B + (2 + qsb) * TILE_B, aoff[es]);
   }
-  const float2 dl_row = lds_at<float2>(lds + 2 * C::STAGE_B + 4 * TILE_B, (qsb * 32 + l32) * 8);
-  const float dsum = dl_row.x, lse2 = dl_row.y;  // D and L of the row
+  // -D and L of the row; -D seeds dP's accumulator (without dropout).
+  const float ndsum = lds_at<float>(lds + 2 * C::STAGE_B + 4 * TILE_B, (qsb * 32 + l32) * 4);
+  const float lse2 = lds_at<float>(lds + 2 * C::STAGE_B + 4 * TILE_B + 256, (qsb * 32 + l32) * 4);
+  f32x16 dinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = DROPOUT ? 0.f : ndsum;
   if (n_it > 1)
     ring_barrier<C::NPAIR_B>();
   else
@@ -541,12 +557,12 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     const bool active = !(j >= kt_end || (CAUSAL && k0 > q0 + 31));
     if (!active && it + 2 < n_it) issue(it + 2);
     if (active) {
-      const unsigned char* st = lds + (it % 3) * C::STAGE_B;
+      const unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
       const unsigned char* tk = st + ST_K + ks * TILE_B;
       const unsigned char* tv = st + ST_V + ks * TILE_B;
 
       // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
-      f32x16 sacc = zero16(), dpacc = zero16();
+      f32x16 sacc = zero16(), dpacc = dinit;
 #pragma unroll
       for (int es = 0; es < NES; ++es) {
         sacc = mfma32x32x16(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
@@ -577,9 +593,9 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
             float x = fmaf(sacc[r], c, -lse2);
             if (MASK) x = (8 * cg + u <= lim) ? x : -INFINITY;
             const float ps = fast_exp2(x);
-            float dp = dpacc[r];
-            if (DROPOUT) dp = ((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f;
-            dsb[r >> 3][r & 7] = (__bf16)(ps * (dp - dsum));
+            float dp = dpacc[r];  // dP - D without dropout
+            if (DROPOUT) dp = (((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f) + ndsum;
+            dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
           }
         }
       };
@@ -643,8 +659,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb)
     role_dq<E, CAUSAL, DROPOUT>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
-// D_i = rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every row.
-// CPR lanes share a row; each loads one 16-byte chunk of dO and of O.
+// -D_i = -rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every
+// row, in two planes of B*H*Sq floats.  CPR lanes share a row; each loads one
+// 16-byte chunk of dO and of O.
 template <int E>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int CPR = E / 8, RPB = 256 / CPR;
@@ -663,10 +680,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
   d = group_sum<CPR>(d);
   if (row < rows && col == 0) {
-    float2 out;
-    out.x = d;
-    out.y = p.lse[row] * kLog2e - __log2f(p.scale);
-    *reinterpret_cast<float2*>(p.dl + row * 2) = out;
+    p.dl[row] = -d;
+    p.dl[rows + row] = p.lse[row] * kLog2e - __log2f(p.scale);
   }
 }
 

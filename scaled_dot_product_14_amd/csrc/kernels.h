@@ -36,7 +36,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   const float* lse;  // contiguous [B, H, Sq]
-  float* dl;         // workspace: (D_i, LSE_i*log2(e) - log2(scale)) per row, [B, H, Sq, 2]
+  float* dl;         // workspace: -D_i plane then LSE_i*log2(e) - log2(scale) plane, each [B, H, Sq]
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Sq, Sk;
   float scale;       // softmax scale
