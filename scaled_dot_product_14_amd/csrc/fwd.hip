@@ -41,6 +41,7 @@
 // stay in that XCD's L2.
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_ring.h"
 
 namespace sdpa14 {
 namespace {
@@ -63,31 +64,32 @@ __device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& 
 
 template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT>
 __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles) {
-  static_assert(E % 32 == 0 && BN % 32 == 0, "tile shape");
+  static_assert(E % 64 == 0 && BN % 32 == 0, "tile shape");
   constexpr int NW = NQ * NS;
-  constexpr int BM = NQ * 32;
-  constexpr int KP = E + 8;   // K tile pitch (elements): conflict-free 16-byte row reads
-  constexpr int VP = E + 32;  // V tile pitch: conflict-free transposed reads
   constexpr int NT = NW * 64;
-  constexpr int ROWS = NS * BN;  // key rows staged per iteration
-  constexpr int CPR = E / 8;     // 16-byte chunks per row
-  constexpr int CHUNKS = ROWS * CPR;
-  constexpr int PER = (CHUNKS + NT - 1) / NT;
+  constexpr int BM = NQ * 32;
+  constexpr int NES = E / 16;
   constexpr int NEB = E / 32;
-  constexpr int KV_BYTES = ROWS * (KP + VP) * 2;
+  constexpr int ROWS = NS * BN;         // key rows staged per iteration
+  constexpr int ROW_B = 2 * E;
+  constexpr int KT_B = ROWS * ROW_B;    // bytes of the K (and of the V) rows of a stage
+  constexpr int STAGE = 2 * KT_B;       // [K rows][V rows], swizzled, unpadded
+  constexpr int NSTAGE = (3 * STAGE <= 64 * 1024) ? 3 : 2;  // keep two workgroups per CU
+  static_assert(KT_B % (NT * 16) == 0, "whole loads per thread");
+  constexpr int NLD = KT_B / (NT * 16);  // loads per thread per tensor per stage
+  constexpr int NPS = 2 * NLD;           // loads per thread per stage
   constexpr int CMB_FLOATS = (NS - 1) * NQ * (NEB * 16 + 2) * 64;  // merge buffer
-  constexpr int LDS_BYTES = KV_BYTES > CMB_FLOATS * 4 ? KV_BYTES : CMB_FLOATS * 4;
+  constexpr int LDS_BYTES =
+      NSTAGE * STAGE > CMB_FLOATS * 4 ? NSTAGE * STAGE : CMB_FLOATS * 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  uint16_t* ks = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* vs = ks + ROWS * KP;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int qs = wave % NQ;  // query sub-tile of this wave
+  const int qs = wave % NQ;   // query sub-tile of this wave
   const int ksp = wave / NQ;  // key share of this wave
 
   int bh, rank;
@@ -111,47 +113,51 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   // Rows past Sq read as zeros through the buffer range check.
   const __amdgpu_buffer_rsrc_t qr =
       make_rsrc(qp, (uint32_t)(((int64_t)(p.Sq - 1) * p.sq.s + E) * 2));
-  bf16x8 qf[E / 16];
+  bf16x8 qf[NES];
 #pragma unroll
-  for (int es = 0; es < E / 16; ++es)
+  for (int es = 0; es < NES; ++es)
     qf[es] = __builtin_bit_cast(
         bf16x8, buffer_load16(qr, (uint32_t)(((int64_t)qrow * p.sq.s + es * 16 + 8 * g) * 2)));
 
-  // K and V rows past kend read as zeros.
+  // K and V rows past kend read as zeros.  Stage it % NSTAGE of the ring holds
+  // key rows it*ROWS .. it*ROWS + ROWS-1, loaded straight into LDS.
   const uint32_t kbytes = (uint32_t)(((int64_t)(kend - 1) * p.sk.s + E) * 2);
   const uint32_t vbytes = (uint32_t)(((int64_t)(kend - 1) * p.sv.s + E) * 2);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, kend > 0 ? kbytes : 0);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, kend > 0 ? vbytes : 0);
   const uint32_t kstride = (uint32_t)(p.sk.s * 2), vstride = (uint32_t)(p.sv.s * 2);
-
-  uint4 kreg[PER], vreg[PER];
-  auto load_rows = [&](int r0) {
+  uint32_t ok[NLD], ov[NLD];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      const uint32_t row = (uint32_t)(r0 + c / CPR), col16 = (uint32_t)(c % CPR) * 16u;
-      kreg[i] = buffer_load16(kr, row * kstride + col16);
-      vreg[i] = buffer_load16(vr, row * vstride + col16);
-    }
-  };
-  auto store_rows = [&]() {
+  for (int k = 0; k < NLD; ++k) {
+    ok[k] = dma_src_offset<E, NT>(k, tid, p.sk.s);
+    ov[k] = dma_src_offset<E, NT>(k, tid, p.sv.s);
+  }
+  auto stage = [&](int it) { return lds + ring_offset<STAGE, NSTAGE>(it); };
+  auto issue = [&](int it) {
+    unsigned char* st = stage(it);
+    const uint32_t r0 = (uint32_t)(it * ROWS);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NT;
-      if (CHUNKS % NT == 0 || c < CHUNKS) {
-        const int row = c / CPR, col = c % CPR;
-        *reinterpret_cast<uint4*>(ks + row * KP + col * 8) = kreg[i];
-        *reinterpret_cast<uint4*>(vs + row * VP + col * 8) = vreg[i];
-      }
+    for (int k = 0; k < NLD; ++k) {
+      dma16(kr, st + k * NT * 16 + wave * 1024, r0 * kstride + ok[k]);
+      dma16(vr, st + KT_B + k * NT * 16 + wave * 1024, r0 * vstride + ov[k]);
     }
   };
 
-  // Transposed-read addressing for the V^T operand (see device_common.h): lane
-  // reads rows 4*g + (lane%16)/4 (+8), columns 16*((lane/16)%2) + 4*(lane%4).
+  // Per-lane LDS offsets.  S^T reads key row ksp*BN + 32*kb + l32 (the A
+  // operand: lane = key, 8 consecutive e per lane); the transposed reads of V^T
+  // map contraction slot (g, i) of 16-key step ksx to key row 16*ksx + 8*(i/4)
+  // + 4*g + i%4 of the share, the C-register order of S^T.
+  int aoff[NES];
+#pragma unroll
+  for (int es = 0; es < NES; ++es) aoff[es] = chunk_off<E>(l32, 2 * es + g) + ksp * BN * ROW_B;
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const uint16_t* kw = ks + ksp * BN * KP + l32 * KP + 8 * g;  // this wave's K rows
-  const uint16_t* vw = vs + ksp * BN * VP + tr_row * VP + tr_col;
+  int troff[2][NEB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int eb = 0; eb < NEB; ++eb)
+      troff[t][eb] = KT_B + ksp * BN * ROW_B + tr_off<E>(8 * t + tr_row, 32 * eb + tr_col);
 
   f32x16 oacc[NEB];
 #pragma unroll
@@ -166,26 +172,32 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   uint64_t drow = 0;
   if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
 
-  load_rows(0);
+  const int npre = min(n_it, NSTAGE - 1);
+  for (int it = 0; it < npre; ++it) issue(it);
+#pragma unroll
+  for (int es = 0; es < NES; ++es) settle(qf[es]);  // waits for the stages too
+  ring_barrier<0>();
+
   for (int it = 0; it < n_it; ++it) {
-    __syncthreads();
-    store_rows();
-    __syncthreads();
-    if (it + 1 < n_it) load_rows((it + 1) * ROWS);
     const int j = it * NS + ksp;
     const int k0 = j * BN;
     // Skip tiles past the key range and, when causal, above the diagonal.
     const bool active = (j < n_kt) && (!CAUSAL || k0 <= q0 + 31);
+    const bool more = it + NSTAGE - 1 < n_it;
+    if (!active && more) issue(it + NSTAGE - 1);
     if (active) {
+      const unsigned char* st = stage(it);
       // S^T for BN keys x 32 queries.
       f32x16 s[BN / 32];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
         s[kb] = zero16();
 #pragma unroll
-        for (int es = 0; es < E / 16; ++es)
-          s[kb] = mfma32x32x16(lds_bf16x8(kw + kb * 32 * KP + es * 16), qf[es], s[kb]);
+        for (int es = 0; es < NES; ++es)
+          s[kb] = mfma32x32x16(lds_at<bf16x8>(st, aoff[es] + kb * 32 * ROW_B), qf[es], s[kb]);
       }
+      // The next stage's loads go out behind the first products.
+      if (more) issue(it + NSTAGE - 1);
 
       if (k0 + BN - 1 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1)) {
         const int lim = key_limit - k0 - 4 * g;  // key offset past which scores are hidden
@@ -216,15 +228,19 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
           for (int r = 0; r < 16; ++r) oacc[eb][r] *= alpha;
       }
 
+      // P (bf16) as the B operand: 16-key step ksx takes registers 8*(ksx%2)..+7
+      // of block ksx/2, i.e. keys 16*ksx + 8*(i/4) + 4*g + i%4 for element i.  The
+      // row sum adds the fp32 probabilities (the log-sum-exp needs them unrounded).
       const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // never -inf - -inf
+      bf16x8 pb[BN / 16];
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
+      for (int ksx = 0; ksx < BN / 16; ++ksx)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(s[kb][r], c, -m_use));
-          s[kb][r] = pv;
+        for (int i = 0; i < 8; ++i) {
+          const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], c, -m_use));
           rs += pv;
+          pb[ksx][i] = (__bf16)pv;
         }
       l_run += rs;
 
@@ -238,34 +254,30 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
             const PhiloxOut w = philox4x32_10(drow + grp, p.drop.seed_lo, p.drop.seed_hi);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-              if (w.w[t] < p.drop.threshold) s[kb][4 * cg + t] = 0.f;
+              if (w.w[t] < p.drop.threshold) pb[2 * kb + (cg >> 1)][4 * (cg & 1) + t] = (__bf16)0.f;
           }
       }
-
-      // P as the B operand: 16-key step ks takes registers 8*(ks%2)..+7 of block
-      // ks/2, i.e. keys 16*ks + 8*(i/4) + 4*g + i%4 for element i.
-      bf16x8 pb[BN / 16];
-#pragma unroll
-      for (int ksx = 0; ksx < BN / 16; ++ksx)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[ksx][i] = (__bf16)s[ksx >> 1][8 * (ksx & 1) + i];
 
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
         for (int ksx = 0; ksx < BN / 16; ++ksx) {
-          const uint16_t* base = vw + ksx * 16 * VP + eb * 32;
-          oacc[eb] = mfma32x32x16(concat(lds_tr4(base), lds_tr4(base + 8 * VP)), pb[ksx],
-                                  oacc[eb]);
+          const int o0 = troff[0][eb] + 16 * ksx * ROW_B, o1 = troff[1][eb] + 16 * ksx * ROW_B;
+          oacc[eb] = mfma32x32x16(tr_pair(st, o0, o1), pb[ksx], oacc[eb]);
         }
     }
+    // The next stage must have landed; this one is free once every wave is past here.
+    if (NSTAGE == 3 && it + 2 < n_it)
+      ring_barrier<NPS>();
+    else
+      ring_barrier<0>();
   }
 
   if (NS > 1) {
-    // Merge the key shares of each query sub-tile into the ksp == 0 wave.
+    // Merge the key shares of each query sub-tile into the ksp == 0 wave (the
+    // loop's last barrier freed the stages).
     float* cmb = reinterpret_cast<float*>(lds);
     constexpr int SLOT = (NEB * 16 + 2) * 64;
-    __syncthreads();  // all waves are done with the K/V tiles
     if (ksp > 0) {
       float* dst = cmb + ((ksp - 1) * NQ + qs) * SLOT;
 #pragma unroll
