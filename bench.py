@@ -55,8 +55,8 @@ def log(msg):
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
-    "fwd": ["fwd.hip", "device_common.h", "philox.h", "kernels.h"],
-    "bwd": ["bwd.hip", "device_common.h", "philox.h", "kernels.h"],
+    "fwd": ["fwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h"],
+    "bwd": ["bwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h"],
 }
 
 
@@ -108,6 +108,23 @@ def timed_loop(fn, steps: int):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps  # ms
+
+
+def capture(step):
+    """HIP graph of one call of step, captured after warm-up on a side stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    return graph
 
 
 def cpu_baseline(w, q, k, v, do, min_seconds: float):
@@ -171,6 +188,8 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(sdpa.sdpa_bwd_workspace_size(w.B, w.H, w.Sq), 256), dtype=torch.uint8,
+                     device="cuda")
     sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset)
     state = {}
 
@@ -181,7 +200,7 @@ def main():
     def bwd():
         s, o = state["so"]
         sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq, dk=dk,
-                      dv=dv)
+                      dv=dv, workspace=ws)
 
     def step():
         fwd()
@@ -192,8 +211,22 @@ def main():
     torch.cuda.synchronize()
     log("warm-up done")
 
-    ms_step = timed_loop(step, args.steps)
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step")
+    # The step's kernels replayed from a HIP graph captured once: the timed work
+    # is the same forward and backward, without the Python launch path.
+    # (With dropout every replay reuses the captured seed and offset.)
+    graph = capture(step)
+    eager = [t.clone() for t in (out, lse, dq, dk, dv)]
+    for t in (out, dq, dk, dv):
+        t.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(eager, (out, lse, dq, dk, dv)))
+    if not same:
+        raise RuntimeError("graph replay differs from the eager step")
+    ms_step = timed_loop(graph.replay, args.steps)
+    log(f"timed {args.steps} graph-replayed steps: {ms_step * 1e3:.2f} us/step")
+    ms_eager = timed_loop(step, args.steps)
+    log(f"timed {args.steps} eager steps: {ms_eager * 1e3:.2f} us/step")
     ms_fwd = timed_loop(fwd, args.steps)
     ms_bwd = timed_loop(bwd, args.steps)
     log(f"fwd {ms_fwd * 1e3:.2f} us, bwd {ms_bwd * 1e3:.2f} us")
@@ -242,6 +275,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "E": w.E,
                    "layout": w.layout, "causal": w.causal, "dropout_p": w.dropout_p,
                    "cache": "warm (same buffers every step)"},
+        "timing": "graph replay of the captured step (eager_ms_per_step: the same step "
+                  "issued from Python each time)",
+        "eager_ms_per_step": ms_eager,
         "fwd": {"tflops": f_fwd / (ms_fwd * 1e-3) / 1e12, "us": ms_fwd * 1e3,
                 "frac_peak": f_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "bwd": {"tflops": f_bwd / (ms_bwd * 1e-3) / 1e12, "us": ms_bwd * 1e3,
