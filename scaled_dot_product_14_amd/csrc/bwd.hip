@@ -199,14 +199,36 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     oq[k] = dma_src_offset<E>(k, tid, p.sq.s);
     odo[k] = dma_src_offset<E>(k, tid, p.sdo.s);
   }
-  auto issue = [&](int it) {
+  // Load idx (0 .. NPAIR_A-1) of stage it: (half, tensor, k) for the Q and dO
+  // tiles, then -D (waves 0, 1) and L (waves 2, 3) of the pair's 64 rows.
+  auto issue_one = [&](int it, int idx, float after) {
     unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
-    issue_tiles<E>(st + ST_Q, wave, (uint32_t)((t0 + 2 * it) * 32), rq, (uint32_t)(p.sq.s * 2),
-                   oq, rdo, (uint32_t)(p.sdo.s * 2), odo);
-    // -D (waves 0, 1) and L (waves 2, 3) of the pair's 64 rows, 4 rows per lane.
-    if (lane < 8)
-      dma16(rdl, st + ST_DL + wave * 128,
-            (uint32_t)((t0 + 2 * it) * 32) * 4u + (uint32_t)((wave & 1) * 128 + lane * 16));
+    const uint32_t row0 = (uint32_t)((t0 + 2 * it) * 32);
+    if (idx < 4 * NLD) {
+      const int half = idx / (2 * NLD), tensor = (idx / NLD) & 1, k = idx % NLD;
+      const uint32_t r = row0 + 32u * half;
+      unsigned char* dst = st + (tensor ? ST_DO : ST_Q) + half * TILE_B + k * 4096 + wave * 1024;
+      if (tensor)
+        dma16_after(rdo, dst, r * (uint32_t)(p.sdo.s * 2) + odo[k], after);
+      else
+        dma16_after(rq, dst, r * (uint32_t)(p.sq.s * 2) + oq[k], after);
+    } else if (lane < 8) {
+      dma16_after(rdl, st + ST_DL + wave * 128,
+                  row0 * 4u + (uint32_t)((wave & 1) * 128 + lane * 16), after);
+    }
+  };
+  // The loads of a stage are spread over the step in NSLOT groups, each placed
+  // after a value of the step's math, so the vector-memory queue drains while
+  // the wave computes (a burst of them stalls the issuing wave).
+  constexpr int NSLOT = 5;
+  auto issue_slot = [&](int it, int slot, float after) {
+#pragma unroll
+    for (int idx = slot * C::NPAIR_A / NSLOT; idx < (slot + 1) * C::NPAIR_A / NSLOT; ++idx)
+      issue_one(it, idx, after);
+  };
+  auto issue = [&](int it) {
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) issue_slot(it, slot, 0.f);
   };
 
   // Per-lane LDS offsets within a tile.  S and dPd read row l32 (the A operand:
@@ -262,9 +284,10 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     const int q0 = (t0 + 2 * it + qs) * 32;
     // Skip tiles past Sq and, when causal, tiles whose rows all precede the keys.
     const bool active = !(q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs));
-    // The next loads are issued after the first products, so that a wave held
-    // up issuing them still has matrix work in flight.
-    if (!active && it + 2 < n_it) issue(it + 2);
+    // Every step issues the loads of stage it+2, also past the last stage (those
+    // rows lie past Sq and read as zeros into a stage nobody reads again), so
+    // the issue points need no branch and every barrier waits the same count.
+    if (!active) issue(it + 2);
     if (active) {
       const unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
       const unsigned char* tq = st + ST_Q + qs * TILE_B;
@@ -287,7 +310,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
         sacc = mfma32x32x16(lds_at<bf16x8>(tq, aoff[es]), kf[es], sacc);
         dpacc = mfma32x32x16(lds_at<bf16x8>(tdo, aoff[es]), vf[es], dpacc);
       }
-      if (it + 2 < n_it) issue(it + 2);
+      issue_slot(it + 2, 0, 0.f);
 
       // C layout: lane = key, register r = row q0 + 8*(r/4) + 4*g + r%4.  Only
       // diagonal and ragged tiles take the masked variant.
@@ -318,6 +341,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
             }
             pb[r >> 3][r & 7] = (__bf16)pd;
             dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
+            if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
           }
         }
       };
@@ -332,14 +356,13 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
           const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
           dva[eb] = mfma32x32x16(tr_pair(tdo, o0, o1), pb[hf], dva[eb]);
           dka[eb] = mfma32x32x16(tr_pair(tq, o0, o1), dsb[hf], dka[eb]);
+          if (hf == 1 && (eb == 0 || eb == NEB - 1)) issue_slot(it + 2, eb == 0 ? 3 : 4, 0.f);
         }
     }
     // Stage it+1 must have landed; stage it is free once every wave is past here.
-    if (it + 2 < n_it)
-      ring_barrier<C::NPAIR_A>();
-    else
-      ring_barrier<0>();
+    ring_barrier<C::NPAIR_A>();
   }
+  ring_barrier<0>();  // the trailing loads have landed before the stages are reused
 
   // dV = (1/scale) * sum(Pd^T dO) since Pd carries the scale; dK carries it already.
   // Wave qs = 0 finalizes the first half of the columns of dV and dK, qs = 1 the rest.
@@ -395,9 +418,27 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     okk[k] = dma_src_offset<E>(k, tid, p.sk.s);
     ov[k] = dma_src_offset<E>(k, tid, p.sv.s);
   }
+  // Load idx (0 .. NPAIR_B-1) of stage it: (half, tensor, k) for the K and V tiles.
+  auto issue_one = [&](int it, int idx, float after) {
+    unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
+    const int half = idx / (2 * NLD), tensor = (idx / NLD) & 1, k = idx % NLD;
+    const uint32_t r = (uint32_t)(64 * it) + 32u * half;
+    unsigned char* dst = st + (tensor ? ST_V : ST_K) + half * TILE_B + k * 4096 + wave * 1024;
+    if (tensor)
+      dma16_after(rvv, dst, r * (uint32_t)(p.sv.s * 2) + ov[k], after);
+    else
+      dma16_after(rk, dst, r * (uint32_t)(p.sk.s * 2) + okk[k], after);
+  };
+  // The loads of a stage are spread over the step in NSLOT groups.
+  constexpr int NSLOT = 4;
+  auto issue_slot = [&](int it, int slot, float after) {
+#pragma unroll
+    for (int idx = slot * C::NPAIR_B / NSLOT; idx < (slot + 1) * C::NPAIR_B / NSLOT; ++idx)
+      issue_one(it, idx, after);
+  };
   auto issue = [&](int it) {
-    issue_tiles<E>(lds + ring_offset<C::STAGE_B>(it) + ST_K, wave, (uint32_t)(64 * it), rk,
-                   (uint32_t)(p.sk.s * 2), okk, rvv, (uint32_t)(p.sv.s * 2), ov);
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) issue_slot(it, slot, 0.f);
   };
 
   int aoff[NES];
@@ -461,7 +502,9 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     const int j = 2 * it + ks;
     const int k0 = j * 32;
     const bool active = !(j >= kt_end || (CAUSAL && k0 > q0 + 31));
-    if (!active && it + 2 < n_it) issue(it + 2);
+    // Loads of stage it+2 on every step, as in the dK/dV role (past the last
+    // stage they fetch rows nobody reads).
+    if (!active) issue(it + 2);
     if (active) {
       const unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
       const unsigned char* tk = st + ST_K + ks * TILE_B;
@@ -474,7 +517,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
         sacc = mfma32x32x16(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
         dpacc = mfma32x32x16(lds_at<bf16x8>(tv, aoff[es]), dof[es], dpacc);
       }
-      if (it + 2 < n_it) issue(it + 2);
+      issue_slot(it + 2, 0, 0.f);
 
       // Only tiles that reach the diagonal or past Sk take the masked variant.
       const bool need_mask = (k0 + 31 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1));
@@ -502,6 +545,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
             float dp = dpacc[r];  // dP - D without dropout
             if (DROPOUT) dp = (((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f) + ndsum;
             dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
+            if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
           }
         }
       };
@@ -516,13 +560,12 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
         for (int hf = 0; hf < 2; ++hf) {
           const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
           dqa[eb] = mfma32x32x16(tr_pair(tk, o0, o1), dsb[hf], dqa[eb]);
+          if (hf == 1 && eb == 0) issue_slot(it + 2, 3, 0.f);
         }
     }
-    if (it + 2 < n_it)
-      ring_barrier<C::NPAIR_B>();
-    else
-      ring_barrier<0>();
+    ring_barrier<C::NPAIR_B>();
   }
+  ring_barrier<0>();  // the trailing loads have landed before the stages are reused
 
   // Wave ks = 0 finalizes the first half of dQ's columns, ks = 1 the rest.
   float* red = reinterpret_cast<float*>(lds);

@@ -53,6 +53,16 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* l
                : "s"(dst), "v"(voff), "s"(r)
                : "m0");
 }
+// The same load, ordered after the computation of `after` (an unused operand),
+// so the compiler cannot hoist it above that point.
+__device__ __forceinline__ void dma16_after(__amdgpu_buffer_rsrc_t r, unsigned char* lds_wave,
+                                            uint32_t voff, float after) {
+  const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(dst), "v"(voff), "s"(r), "v"(after)
+               : "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int rows,

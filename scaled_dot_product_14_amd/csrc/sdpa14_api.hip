@@ -90,10 +90,11 @@ bool same_shape(const Desc& a, const Desc& b) {
 }
 
 // Kernels read rows of one (batch, head) slice through 32-bit buffer offsets.
-// Kernels address a (batch, head) slice with 32-bit byte offsets, including the
-// rows of a tile that run past S (up to 127 of them; those read as zeros).
+// Kernels address a (batch, head) slice with 32-bit byte offsets, including
+// rows past S that tiles and trailing ring loads reach (fewer than 256; those
+// read as zeros through the buffer range check).
 bool slice_ok(const Desc& t) {
-  return (t.S + 127) * t.st.s * 2 + t.E * 2 < (int64_t(1) << 31);
+  return (t.S + 255) * t.st.s * 2 + t.E * 2 < (int64_t(1) << 31);
 }
 
 int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
