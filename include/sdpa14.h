@@ -113,6 +113,53 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
              const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
              void* workspace, size_t workspace_bytes, sdpa_stream_t stream);
 
+/*
+ * Options of the extended calls (a NULL pointer to them means none).
+ *
+ *   head_offset, heads_total
+ *       Sharding the heads (the nvFuser PR "DID loop split for SDPA" splits the
+ *       head dimension over devices and keeps dropout_p = 0 pending sharded
+ *       dropout).  The call's head h of batch b is global head head_offset + h
+ *       of a problem with heads_total heads (0 means the call's own H), so the
+ *       keep bits are those of element (b, head_offset + h, i, j) of the whole
+ *       problem: g = ((b*heads_total + head_offset + h)*Sq + i) * ceil(Sk/4) + j/4.
+ *       A forward with dropout advances the offset by B*heads_total*Sq*ceil(Sk/4),
+ *       as the unsharded call would, so shards stay in step.  Requires
+ *       head_offset >= 0, heads_total >= head_offset + H, B*heads_total < 2^31.
+ *   rng_state, rng_used  (device pointers to {seed, offset}, 8-byte aligned)
+ *       Device-resident RNG state for calls inside a captured HIP graph (the
+ *       PyTorch PR "REDO of dropout support for mem eff", Summary: the RNG state
+ *       passed from forward to backward so that graph capture works).
+ *       Forward: rng_state and rng_used are both given or both NULL, and are
+ *       distinct.  When given and dropout_p > 0, a one-thread kernel on `stream`
+ *       first copies rng_state to rng_used and advances rng_state's offset by
+ *       the amount above; the forward then draws its mask from rng_used.  The
+ *       library's host state is neither read nor advanced, and the host outputs
+ *       seed and offset are not written.  With dropout_p == 0 nothing is
+ *       enqueued for the RNG.  Backward: when rng_used is given, (seed, offset)
+ *       are read from it on the device and the host arguments are ignored;
+ *       rng_state is ignored.  Both buffers are caller-owned device memory that
+ *       must stay valid until the work on `stream` is done.
+ */
+typedef struct sdpa_ext {
+  int64_t head_offset;
+  int64_t heads_total;
+  uint64_t* rng_state;
+  uint64_t* rng_used;
+} sdpa_ext;
+
+/* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL. */
+int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                 double dropout_p, int is_causal, double scale,
+                 const sdpa_tensor* out, float* lse,
+                 uint64_t* seed, uint64_t* offset, const sdpa_ext* ext, sdpa_stream_t stream);
+int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+                 const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
+                 double dropout_p, int is_causal, uint64_t seed, uint64_t offset, double scale,
+                 const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
+                 void* workspace, size_t workspace_bytes, const sdpa_ext* ext,
+                 sdpa_stream_t stream);
+
 /* Workspace bytes sdpa_bwd needs for B*H*Sq query rows (8 per row, rounded up to
  * 256); 0 when a size is not positive. */
 size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq);

@@ -7,6 +7,8 @@ declared in ``include/sdpa14.h``); this package is its thin Python binding.
     dq, dk, dv = sdpa_bwd(dout, q, k, v, out, lse, dropout_p, is_causal, seed, offset, scale)
 
 Tensors are bf16, logical [B, H, S, E], BHSE or BSHE stride order, E in {64, 128}.
+``sdpa_fwd_ext`` / ``sdpa_bwd_ext`` add head sharding of the dropout stream and
+a device-resident RNG state for captured graphs.
 """
 
 from ._binding import (  # noqa: F401
@@ -18,9 +20,11 @@ from ._binding import (  # noqa: F401
     describe,
     load_library,
     sdpa_bwd,
+    sdpa_bwd_ext,
     sdpa_bwd_workspace_size,
     sdpa_debug_dropout_mask,
     sdpa_fwd,
+    sdpa_fwd_ext,
     sdpa_get_rng_state,
     sdpa_profile_enable,
     sdpa_profile_read,

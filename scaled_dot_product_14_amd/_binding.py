@@ -27,7 +27,8 @@ KERNEL_FWD = 0
 KERNEL_BWD = 1
 
 EXPORTED = (
-    "sdpa_fwd", "sdpa_bwd", "sdpa_bwd_workspace_size", "sdpa_set_rng_state",
+    "sdpa_fwd", "sdpa_bwd", "sdpa_fwd_ext", "sdpa_bwd_ext", "sdpa_bwd_workspace_size",
+    "sdpa_set_rng_state",
     "sdpa_get_rng_state", "sdpa_status_string", "sdpa_last_error",
     "sdpa_debug_dropout_mask", "sdpa_profile_enable", "sdpa_profile_read",
 )
@@ -39,6 +40,15 @@ class SdpaTensor(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("size", ctypes.c_int64 * 4),
         ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+class SdpaExt(ctypes.Structure):
+    _fields_ = [
+        ("head_offset", ctypes.c_int64),
+        ("heads_total", ctypes.c_int64),
+        ("rng_state", ctypes.c_void_p),
+        ("rng_used", ctypes.c_void_p),
     ]
 
 
@@ -68,6 +78,14 @@ def load_library(path: str = LIB_PATH):
                              ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, P, P, P,
                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.sdpa_bwd.restype = ctypes.c_int
+    E = ctypes.POINTER(SdpaExt)
+    lib.sdpa_fwd_ext.argtypes = [P, P, P, ctypes.c_double, ctypes.c_int, ctypes.c_double, P,
+                                 ctypes.c_void_p, u64p, u64p, E, ctypes.c_void_p]
+    lib.sdpa_fwd_ext.restype = ctypes.c_int
+    lib.sdpa_bwd_ext.argtypes = [P, P, P, P, P, ctypes.c_void_p, ctypes.c_double, ctypes.c_int,
+                                 ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, P, P, P,
+                                 ctypes.c_void_p, ctypes.c_size_t, E, ctypes.c_void_p]
+    lib.sdpa_bwd_ext.restype = ctypes.c_int
     lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_set_rng_state.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
@@ -177,6 +195,85 @@ def sdpa_bwd(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: i
                           _scale_arg(scale), *(ctypes.byref(d) for d in descs[5:]),
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                           _stream(q.device))
+    _check(rc)
+    return dq, dk, dv
+
+
+def _rng_buffer(t, name: str):
+    if t is None:
+        return None
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype in (torch.int64, torch.uint64)
+            and t.numel() == 2 and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device int64 tensor of 2 elements "
+                         "(seed, offset)")
+    return t.data_ptr()
+
+
+def _ext(head_offset, heads_total, rng_state, rng_used) -> SdpaExt:
+    e = SdpaExt()
+    e.head_offset = int(head_offset)
+    e.heads_total = int(heads_total)
+    e.rng_state = _rng_buffer(rng_state, "rng_state")
+    e.rng_used = _rng_buffer(rng_used, "rng_used")
+    return e
+
+
+def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
+                 out=None, lse=None, *, head_offset: int = 0, heads_total: int = 0,
+                 rng_state=None, rng_used=None):
+    """Forward with options: returns ``(out, lse, seed, offset)``.
+
+    ``head_offset`` / ``heads_total`` place the call's heads in a larger problem
+    for the dropout stream.  ``rng_state`` and ``rng_used`` (device int64
+    tensors of two elements, {seed, offset}) keep the RNG state on the device;
+    then ``seed`` and ``offset`` are returned as None and the values the call
+    used land in ``rng_used``.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    dq_, dk_, dv_, do_ = describe(q), describe(k), describe(v), describe(out)
+    ext = _ext(head_offset, heads_total, rng_state, rng_used)
+    seed, offset = ctypes.c_uint64(), ctypes.c_uint64()
+    with torch.cuda.device(q.device):
+        rc = lib.sdpa_fwd_ext(ctypes.byref(dq_), ctypes.byref(dk_), ctypes.byref(dv_),
+                              float(dropout_p), int(bool(is_causal)), _scale_arg(scale),
+                              ctypes.byref(do_), lse.data_ptr(), ctypes.byref(seed),
+                              ctypes.byref(offset), ctypes.byref(ext), _stream(q.device))
+    _check(rc)
+    if rng_state is not None:
+        return out, lse, None, None
+    return out, lse, seed.value, offset.value
+
+
+def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int = 0,
+                 offset: int = 0, scale=None, dq=None, dk=None, dv=None, workspace=None, *,
+                 head_offset: int = 0, heads_total: int = 0, rng_used=None):
+    """Backward with options (see ``sdpa_fwd_ext``): returns ``(dq, dk, dv)``.
+
+    With ``rng_used`` the kernels read (seed, offset) from that device tensor
+    and ``seed`` / ``offset`` are ignored.
+    """
+    lib = load_library()
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    B, H, Sq = q.shape[0], q.shape[1], q.shape[2]
+    if workspace is None:
+        workspace = torch.empty(max(lib.sdpa_bwd_workspace_size(B, H, Sq), 256),
+                                dtype=torch.uint8, device=q.device)
+    descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
+    ext = _ext(head_offset, heads_total, None, rng_used)
+    with torch.cuda.device(q.device):
+        rc = lib.sdpa_bwd_ext(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
+                              float(dropout_p), int(bool(is_causal)), int(seed), int(offset),
+                              _scale_arg(scale), *(ctypes.byref(d) for d in descs[5:]),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              ctypes.byref(ext), _stream(q.device))
     _check(rc)
     return dq, dk, dv
 

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsdpa14.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["sdpa14_api.hip", "fwd.hip", "bwd.hip", "mask.hip"]
+SOURCES = ["sdpa14_api.hip", "fwd.hip", "bwd.hip", "mask.hip", "rng.hip"]
 
 ARCH = "gfx950"
 # Device code: packed fp32 VALU instructions are switched off; MFMA accumulators

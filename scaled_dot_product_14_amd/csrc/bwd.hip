@@ -87,16 +87,17 @@ __device__ __forceinline__ void issue_tiles(unsigned char* st, int wave, uint32_
   }
 }
 
-// Dropout keep bits for the dK/dV role.  The lane holds key `key` (key % 4 ==
+// Dropout keep bits for the dK/dV role (bhg: the global head, dropout_head).
+// The lane holds key `key` (key % 4 ==
 // lane % 4) and, for register group c, the four rows row0 + u, u = 0..3.  Lane t
 // of each quad evaluates the Philox call of row row0 + t for the key group of
 // the quad (four words: keys 4*(key/4) + 0..3), packs the four keep bits, and
 // every lane collects its own key's bit from the four lanes of its quad.
 // Returns bit u = keep(row0 + u, key).
-__device__ __forceinline__ uint32_t keep_bits_for_key(const DropoutParams& d, int bh, int Sq,
+__device__ __forceinline__ uint32_t keep_bits_for_key(const DropoutParams& d, int bhg, int Sq,
                                                       int sk4, int row0, int key, int lane) {
   const int t = lane & 3;
-  const uint64_t ctr = philox_row_base(d, bh, Sq, row0 + t, sk4) + (uint32_t)(key >> 2);
+  const uint64_t ctr = philox_row_base(d, bhg, Sq, row0 + t, sk4) + (uint32_t)(key >> 2);
   const PhiloxOut w = philox4x32_10(ctr, d.seed_lo, d.seed_hi);
   const int nib = (w.w[0] >= d.threshold ? 1 : 0) | (w.w[1] >= d.threshold ? 2 : 0) |
                   (w.w[2] >= d.threshold ? 4 : 0) | (w.w[3] >= d.threshold ? 8 : 0);
@@ -171,6 +172,9 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const int kbs = kb0 + 32 * sb;  // first key of this wave's sub-block
   const int key = kbs + l32;
   const float c = p.scale_log2;
+  DropoutParams drop = p.drop;
+  if (DROPOUT) load_dropout_state(drop);
+  const int bhg = dropout_head(drop, b, h);
 
   const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, E);
   const __amdgpu_buffer_rsrc_t rdo =
@@ -322,7 +326,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
         for (int cg = 0; cg < 4; ++cg) {
           uint32_t kbits = 0xF;
           if (DROPOUT)
-            kbits = keep_bits_for_key(p.drop, bh, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
+            kbits = keep_bits_for_key(drop, bhg, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * cg + u;
@@ -336,8 +340,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
             float dp = dpacc[r], pd = ps;  // dp = dPd - D without dropout
             if (DROPOUT) {
               const bool keep = (kbits >> u) & 1;
-              pd = keep ? ps * p.drop.keep_scale : 0.f;
-              dp = (keep ? dp * p.drop.keep_scale : 0.f) + nd4[cg][u];
+              pd = keep ? ps * drop.keep_scale : 0.f;
+              dp = (keep ? dp * drop.keep_scale : 0.f) + nd4[cg][u];
             }
             pb[r >> 3][r & 7] = (__bf16)pd;
             dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
@@ -454,7 +458,11 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int key_limit = CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1;
   const int sk4 = (p.Sk + 3) >> 2;
   uint64_t drow = 0;
-  if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
+  DropoutParams drop = p.drop;
+  if (DROPOUT) {
+    load_dropout_state(drop);
+    drow = philox_row_base(drop, dropout_head(drop, b, h), p.Sq, qrow, sk4);
+  }
 
   // Q and dO of the block pass through stage 2 (first refilled by iteration 0)
   // together with the first two stages; each wave then takes its rows'
@@ -530,11 +538,11 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
           uint32_t kbits = 0xF;
           if (DROPOUT) {
             const PhiloxOut w = philox4x32_10(drow + (uint32_t)(k0 >> 2) + 2 * cg + g,
-                                              p.drop.seed_lo, p.drop.seed_hi);
-            kbits = (w.w[0] >= p.drop.threshold ? 1u : 0u) |
-                    (w.w[1] >= p.drop.threshold ? 2u : 0u) |
-                    (w.w[2] >= p.drop.threshold ? 4u : 0u) |
-                    (w.w[3] >= p.drop.threshold ? 8u : 0u);
+                                              drop.seed_lo, drop.seed_hi);
+            kbits = (w.w[0] >= drop.threshold ? 1u : 0u) |
+                    (w.w[1] >= drop.threshold ? 2u : 0u) |
+                    (w.w[2] >= drop.threshold ? 4u : 0u) |
+                    (w.w[3] >= drop.threshold ? 8u : 0u);
           }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
@@ -543,7 +551,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
             if (MASK) x = (8 * cg + u <= lim) ? x : -INFINITY;
             const float ps = fast_exp2(x);
             float dp = dpacc[r];  // dP - D without dropout
-            if (DROPOUT) dp = (((kbits >> u) & 1) ? dp * p.drop.keep_scale : 0.f) + ndsum;
+            if (DROPOUT) dp = (((kbits >> u) & 1) ? dp * drop.keep_scale : 0.f) + ndsum;
             dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
             if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
           }

@@ -170,7 +170,10 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 
   const int sk4 = (p.Sk + 3) >> 2;
   uint64_t drow = 0;
-  if (DROPOUT) drow = philox_row_base(p.drop, bh, p.Sq, qrow, sk4);
+  if (DROPOUT) {
+    load_dropout_state(p.drop);
+    drow = philox_row_base(p.drop, dropout_head(p.drop, b, h), p.Sq, qrow, sk4);
+  }
 
   const int npre = min(n_it, NSTAGE - 1);
   for (int it = 0; it < npre; ++it) issue(it);

@@ -63,5 +63,8 @@ hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
 hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream);
+// One thread: used[0..1] = state[0..1], then state[1] += advance.
+hipError_t launch_rng_step(uint64_t* state, uint64_t* used, uint64_t advance,
+                           hipStream_t stream);
 
 }  // namespace sdpa14

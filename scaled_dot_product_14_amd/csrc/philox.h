@@ -11,7 +11,10 @@
 // stream by the absolute position of each score element.  Here one call
 // covers four consecutive keys j = 4c..4c+3 of query row i of head (b, h):
 // counter = offset + ((b*H + h)*Sq + i) * ceil(Sk/4) + c, key = seed, and key
-// j takes output word j % 4.  An element is kept iff its word is >= the
+// j takes output word j % 4.  For a call on a slice of the heads, H is the
+// head count of the whole problem and h the global head index, the sharded
+// dropout the nvFuser PR "DID loop split for SDPA" leaves open (its test keeps
+// p = 0 pending sharded dropout support).  An element is kept iff its word is >= the
 // threshold floor(p * 2^32).
 #pragma once
 
@@ -55,17 +58,38 @@ __device__ __forceinline__ PhiloxOut philox4x32_10(uint64_t counter, uint32_t k0
 
 // Dropout parameters shared by the kernels.
 struct DropoutParams {
-  uint64_t offset;     // Philox offset of this forward call
-  uint32_t seed_lo;    // key word 0
-  uint32_t seed_hi;    // key word 1
-  uint32_t threshold;  // floor(p * 2^32); keep iff word >= threshold
-  float keep_scale;    // 1 / (1 - p), rounded to fp32 on the host
+  uint64_t offset;        // Philox offset of this forward call
+  uint32_t seed_lo;       // key word 0
+  uint32_t seed_hi;       // key word 1
+  uint32_t threshold;     // floor(p * 2^32); keep iff word >= threshold
+  float keep_scale;       // 1 / (1 - p), rounded to fp32 on the host
+  int32_t heads_total;    // heads of the unsharded problem (the call's H when not sharded)
+  int32_t head_offset;    // global index of the call's head 0
+  const uint64_t* state;  // device {seed, offset} of the call, or null: the fields above
 };
 
-// Counter of query row `row` of head `bh` for key group 0; key group c adds c.
-__device__ __forceinline__ uint64_t philox_row_base(const DropoutParams& d, int bh, int Sq,
+// Global index, in the random stream, of the call's head h of batch b.  A call
+// on a slice of the heads then draws the mask the whole problem would.
+__device__ __forceinline__ int dropout_head(const DropoutParams& d, int b, int h) {
+  return b * d.heads_total + d.head_offset + h;
+}
+
+// Takes seed and offset from device memory when the call keeps them there
+// (a captured graph then draws fresh bits on every replay).
+__device__ __forceinline__ void load_dropout_state(DropoutParams& d) {
+  if (d.state != nullptr) {
+    const uint64_t seed = d.state[0], offset = d.state[1];
+    d.seed_lo = static_cast<uint32_t>(seed);
+    d.seed_hi = static_cast<uint32_t>(seed >> 32);
+    d.offset = offset;
+  }
+}
+
+// Counter of query row `row` of global head `bhg` (dropout_head) for key group
+// 0; key group c adds c.
+__device__ __forceinline__ uint64_t philox_row_base(const DropoutParams& d, int bhg, int Sq,
                                                     int row, int sk4) {
-  return d.offset + (static_cast<uint64_t>(bh) * static_cast<uint64_t>(Sq) +
+  return d.offset + (static_cast<uint64_t>(bhg) * static_cast<uint64_t>(Sq) +
                      static_cast<uint64_t>(row)) * static_cast<uint64_t>(sk4);
 }
 

@@ -131,14 +131,52 @@ int resolve_scale(double scale, int64_t E, float* out) {
   return SDPA_OK;
 }
 
-DropoutParams make_dropout(double p, uint64_t seed, uint64_t offset) {
+DropoutParams make_dropout(double p, uint64_t seed, uint64_t offset, int64_t heads_total,
+                           int64_t head_offset, const uint64_t* state) {
   DropoutParams d;
   d.offset = offset;
   d.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   d.seed_hi = (uint32_t)(seed >> 32);
   d.threshold = (uint32_t)floor(p * 4294967296.0);
   d.keep_scale = (float)(1.0 / (1.0 - p));
+  d.heads_total = (int32_t)heads_total;
+  d.head_offset = (int32_t)head_offset;
+  d.state = state;
   return d;
+}
+
+// Resolved extension options of one call.
+struct Ext {
+  int64_t head_offset = 0;
+  int64_t heads_total = 0;  // the call's H when not sharded
+  uint64_t* rng_state = nullptr;
+  uint64_t* rng_used = nullptr;
+};
+
+int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, bool forward, Ext* out) {
+  Ext e;
+  e.heads_total = H;
+  if (ext != nullptr) {
+    if (ext->head_offset < 0) return fail(SDPA_ERR_INVALID, "head_offset < 0");
+    e.head_offset = ext->head_offset;
+    e.heads_total = ext->heads_total == 0 ? H : ext->heads_total;
+    if (e.heads_total < e.head_offset + H)
+      return fail(SDPA_ERR_INVALID, "heads_total (%lld) < head_offset + H (%lld)",
+                  (long long)e.heads_total, (long long)(e.head_offset + H));
+    if (B * e.heads_total > kMaxGrid)
+      return fail(SDPA_ERR_UNSUPPORTED, "B * heads_total too large");
+    e.rng_state = forward ? ext->rng_state : nullptr;
+    e.rng_used = ext->rng_used;
+    if (forward && (e.rng_state == nullptr) != (e.rng_used == nullptr))
+      return fail(SDPA_ERR_INVALID, "rng_state and rng_used go together");
+    for (const uint64_t* ptr : {(const uint64_t*)e.rng_state, (const uint64_t*)e.rng_used})
+      if (reinterpret_cast<uintptr_t>(ptr) % 8 != 0)
+        return fail(SDPA_ERR_UNSUPPORTED, "device RNG buffers must be 8-byte aligned");
+    if (e.rng_state != nullptr && e.rng_state == e.rng_used)
+      return fail(SDPA_ERR_INVALID, "rng_state and rng_used must be distinct buffers");
+  }
+  *out = e;
+  return SDPA_OK;
 }
 
 uint64_t offset_advance(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
@@ -200,6 +238,14 @@ extern "C" {
 int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
              double dropout_p, int is_causal, double scale, const sdpa_tensor* out, float* lse,
              uint64_t* seed, uint64_t* offset, sdpa_stream_t stream) {
+  return sdpa_fwd_ext(q, k, v, dropout_p, is_causal, scale, out, lse, seed, offset, nullptr,
+                      stream);
+}
+
+int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
+                 double dropout_p, int is_causal, double scale, const sdpa_tensor* out,
+                 float* lse, uint64_t* seed, uint64_t* offset, const sdpa_ext* ext,
+                 sdpa_stream_t stream) {
   Desc dq, dk, dv, dout;
   int rc;
   if ((rc = check_tensor(q, "q", &dq))) return rc;
@@ -214,16 +260,26 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
   if ((rc = check_dropout(dropout_p))) return rc;
   float sc;
   if ((rc = resolve_scale(scale, dq.E, &sc))) return rc;
+  Ext e;
+  if ((rc = check_ext(ext, dq.B, dq.H, true, &e))) return rc;
+  const bool drop = dropout_p > 0.0;
+  const uint64_t advance = offset_advance(dq.B, e.heads_total, dq.S, dk.S);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
 
-  uint64_t s0, o0;
-  {
+  uint64_t s0 = 0, o0 = 0;
+  if (e.rng_state == nullptr) {
     std::lock_guard<std::mutex> lk(g_rng_mu);
     s0 = g_rng_seed;
     o0 = g_rng_offset;
-    if (dropout_p > 0.0) g_rng_offset += offset_advance(dq.B, dq.H, dq.S, dk.S);
+    if (drop) g_rng_offset += advance;
   }
-  if (seed) *seed = s0;
-  if (offset) *offset = o0;
+  if (e.rng_state == nullptr && seed) *seed = s0;
+  if (e.rng_state == nullptr && offset) *offset = o0;
+  (void)hipGetLastError();
+  if (drop && e.rng_state != nullptr) {
+    const hipError_t err = launch_rng_step(e.rng_state, e.rng_used, advance, st);
+    if (err != hipSuccess) return hip_status(err, "RNG state launch");
+  }
 
   FwdParams p;
   p.q = dq.ptr;
@@ -240,11 +296,9 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
   p.Sq = (int)dq.S;
   p.Sk = (int)dk.S;
   p.scale_log2 = sc * 1.44269504088896340736f;
-  p.drop = make_dropout(dropout_p, s0, o0);
-  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
+  p.drop = make_dropout(dropout_p, s0, o0, e.heads_total, e.head_offset, e.rng_used);
   const hipError_t err = timed_launch(SDPA_KERNEL_FWD, st, [&] {
-    return launch_fwd(p, (int)dq.E, is_causal != 0, dropout_p > 0.0, tile_choice(), st);
+    return launch_fwd(p, (int)dq.E, is_causal != 0, drop, tile_choice(), st);
   });
   return hip_status(err, "forward launch");
 }
@@ -254,6 +308,16 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
              int is_causal, uint64_t seed, uint64_t offset, double scale, const sdpa_tensor* dq,
              const sdpa_tensor* dk, const sdpa_tensor* dv, void* workspace,
              size_t workspace_bytes, sdpa_stream_t stream) {
+  return sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p, is_causal, seed, offset, scale, dq, dk,
+                      dv, workspace, workspace_bytes, nullptr, stream);
+}
+
+int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+                 const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
+                 double dropout_p, int is_causal, uint64_t seed, uint64_t offset, double scale,
+                 const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
+                 void* workspace, size_t workspace_bytes, const sdpa_ext* ext,
+                 sdpa_stream_t stream) {
   Desc ddo, dqi, dki, dvi, dout_i, dqo, dko, dvo;
   int rc;
   if ((rc = check_tensor(dout, "dout", &ddo))) return rc;
@@ -283,6 +347,8 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
     return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (workspace_bytes < bwd_workspace_bytes(dqi.B, dqi.H, dqi.S))
     return fail(SDPA_ERR_WORKSPACE, "workspace is smaller than sdpa_bwd_workspace_size()");
+  Ext e;
+  if ((rc = check_ext(ext, dqi.B, dqi.H, false, &e))) return rc;
 
   BwdParams p;
   p.q = dqi.ptr;
@@ -309,7 +375,7 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   p.Sk = (int)dki.S;
   p.scale = sc;
   p.scale_log2 = sc * 1.44269504088896340736f;
-  p.drop = make_dropout(dropout_p, seed, offset);
+  p.drop = make_dropout(dropout_p, seed, offset, e.heads_total, e.head_offset, e.rng_used);
   const int E = (int)dqi.E;
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -366,7 +432,7 @@ int sdpa_debug_dropout_mask(uint64_t seed, uint64_t offset, double dropout_p, in
   p.H = (int)H;
   p.Sq = (int)Sq;
   p.Sk = (int)Sk;
-  p.drop = make_dropout(dropout_p, seed, offset);
+  p.drop = make_dropout(dropout_p, seed, offset, H, 0, nullptr);
   (void)hipGetLastError();
   return hip_status(launch_mask(p, reinterpret_cast<hipStream_t>(stream)), "mask launch");
 }

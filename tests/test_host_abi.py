@@ -138,6 +138,49 @@ def test_backward_checks_workspace(lib, kw, needle):
     assert bnd.sdpa_get_rng_state() == (7, 8)
 
 
+def _ext(head_offset=0, heads_total=0, rng_state=None, rng_used=None):
+    e = bnd.SdpaExt()
+    e.head_offset, e.heads_total, e.rng_state, e.rng_used = head_offset, heads_total, rng_state, rng_used
+    return e
+
+
+@pytest.mark.parametrize("ext,code,needle", [
+    (_ext(head_offset=-1), bnd.SDPA_ERR_INVALID, "head_offset"),
+    (_ext(head_offset=1, heads_total=2), bnd.SDPA_ERR_INVALID, "heads_total"),
+    (_ext(heads_total=1), bnd.SDPA_ERR_INVALID, "heads_total"),
+    (_ext(heads_total=1 << 31), bnd.SDPA_ERR_UNSUPPORTED, "too large"),
+    (_ext(rng_state=FAKE), bnd.SDPA_ERR_INVALID, "together"),
+    (_ext(rng_used=FAKE), bnd.SDPA_ERR_INVALID, "together"),
+    (_ext(rng_state=FAKE, rng_used=FAKE), bnd.SDPA_ERR_INVALID, "distinct"),
+    (_ext(rng_state=FAKE + 4, rng_used=FAKE + 64), bnd.SDPA_ERR_UNSUPPORTED, "aligned"),
+])
+def test_forward_ext_rejects_bad_options(lib, ext, code, needle):
+    bnd.sdpa_set_rng_state(31, 41)
+    q, k, v, out = _t(), _t(), _t(), _t()
+    s, o = ctypes.c_uint64(), ctypes.c_uint64()
+    rc = lib.sdpa_fwd_ext(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0.1, 1, math.nan,
+                          ctypes.byref(out), FAKE, ctypes.byref(s), ctypes.byref(o),
+                          ctypes.byref(ext), None)
+    assert rc == code, (rc, _err(lib))
+    assert needle.lower() in _err(lib).lower()
+    assert bnd.sdpa_get_rng_state() == (31, 41)
+
+
+@pytest.mark.parametrize("ext,code,needle", [
+    (_ext(head_offset=-3), bnd.SDPA_ERR_INVALID, "head_offset"),
+    (_ext(head_offset=2, heads_total=3), bnd.SDPA_ERR_INVALID, "heads_total"),
+    (_ext(rng_used=FAKE + 2), bnd.SDPA_ERR_UNSUPPORTED, "aligned"),
+])
+def test_backward_ext_rejects_bad_options(lib, ext, code, needle):
+    t = {n: _t() for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
+    rc = lib.sdpa_bwd_ext(*(ctypes.byref(t[n]) for n in ("dout", "q", "k", "v", "out")),
+                          FAKE, 0.1, 1, 0, 0, math.nan,
+                          *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")),
+                          FAKE, WS_BYTES, ctypes.byref(ext), None)
+    assert rc == code, (rc, _err(lib))
+    assert needle.lower() in _err(lib).lower()
+
+
 def test_workspace_size():
     # 8 bytes per query row (D and the base-2 LSE), rounded up to 256 bytes.
     assert sdpa.sdpa_bwd_workspace_size(1, 2, 128) == 2048
