@@ -27,6 +27,14 @@ struct PhiloxOut {
   uint32_t w[4];
 };
 
+// a ^ b ^ k in one VALU instruction (three-input bitwise op, truth table 0x96);
+// k is wave-uniform (a key word).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
 __device__ __forceinline__ PhiloxOut philox4x32_10(uint64_t counter, uint32_t k0, uint32_t k1) {
   constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
   constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
@@ -43,8 +51,8 @@ __device__ __forceinline__ PhiloxOut philox4x32_10(uint64_t counter, uint32_t k0
     const uint64_t p0 = static_cast<uint64_t>(kM0) * c0, p1 = static_cast<uint64_t>(kM1) * c2;
     const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
     const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
-    const uint32_t n0 = hi1 ^ c1 ^ k0;
-    const uint32_t n2 = hi0 ^ c3 ^ k1;
+    const uint32_t n0 = xor3(hi1, c1, k0);
+    const uint32_t n2 = xor3(hi0, c3, k1);
     c0 = n0;
     c1 = lo1;
     c2 = n2;
