@@ -21,7 +21,11 @@ Steps, per head, with s the scale:
 
 1. ``scale=None`` means 1/sqrt(E) (the PR passes ``None``; reading: the usual
    SDPA default).
-2. S = s * Q K^T, shape [Sq, Sk].
+2. S = s * Q K^T (+ bias), shape [Sq, Sk].  The optional additive bias is the
+   relative-position term the forum thread's opening question asks SDPA to
+   accept and the attn_bias support the PyTorch PR "REDO of dropout support
+   for mem eff" announces for the memory-efficient kernel; reading: it is added
+   to the scaled scores before masking, and a -inf entry hides its key.
 3. valid(i, j) = j <= i when causal (reading: top-left alignment, the plain
    lower-triangular mask; it also holds when Sq != Sk), else everywhere.
 4. LSE_i = m_i + ln sum_{valid j} exp(S_ij - m_i), m_i the row max over valid
@@ -82,9 +86,11 @@ def _as64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def head_forward(qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray):
+def head_forward(qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray, bias_h=None):
     """Steps 2, 4, 5, 7 on one head.  Returns (O [Sq,E], LSE [Sq], P [Sq,Sk])."""
     S = s * (qh @ kh.T)
+    if bias_h is not None:
+        S = S + bias_h
     masked = np.where(valid, S, -np.inf)
     m = masked.max(axis=1)
     lse = m + np.log(np.exp(masked - m[:, None]).sum(axis=1))
@@ -93,9 +99,10 @@ def head_forward(qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray):
     return out, lse, P
 
 
-def head_backward(dOh, qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray):
-    """Steps 2-8 on one head.  Returns (dQ, dK, dV, D)."""
-    _, _, P = head_forward(qh, kh, vh, s, valid, mult)
+def head_backward(dOh, qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray, bias_h=None):
+    """Steps 2-8 on one head.  Returns (dQ, dK, dV, D).  The bias enters through
+    P only: S = s Q K^T + bias, so dQ and dK keep their form."""
+    _, _, P = head_forward(qh, kh, vh, s, valid, mult, bias_h)
     dPd = dOh @ vh.T
     dP = dPd * mult
     D = (P * dP).sum(axis=1)
@@ -110,28 +117,38 @@ def _heads(B: int, H: int, heads):
     return [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
 
 
+def _bias64(bias, B: int, H: int, Sq: int, Sk: int):
+    """The bias as float64 broadcast to [B, H, Sq, Sk], or None."""
+    if bias is None:
+        return None
+    return np.broadcast_to(_as64(bias), (B, H, Sq, Sk))
+
+
 def fwd(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
-        seed: int = 0, offset: int = 0, heads=None):
+        seed: int = 0, offset: int = 0, heads=None, bias=None):
     """Forward on logical [B, H, S, E] inputs.
 
     Returns ``(out [B,H,Sq,E], lse [B,H,Sq])`` in float64.  With ``heads`` (a
     list of (b, h)) only those heads are computed and the rest are NaN.
+    ``bias`` (optional) broadcasts to [B, H, Sq, Sk].
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, Sq, E = q.shape
     Sk = k.shape[2]
     s = resolve_scale(scale, E)
+    bias = _bias64(bias, B, H, Sq, Sk)
     out = np.full((B, H, Sq, v.shape[3]), np.nan)
     lse = np.full((B, H, Sq), np.nan)
     valid = valid_mask(Sq, Sk, is_causal)
     for b, h in _heads(B, H, heads):
         mult = dropout_multiplier(dropout_p, seed, offset, B, H, Sq, Sk, b, h)
-        out[b, h], lse[b, h], _ = head_forward(q[b, h], k[b, h], v[b, h], s, valid, mult)
+        out[b, h], lse[b, h], _ = head_forward(q[b, h], k[b, h], v[b, h], s, valid, mult,
+                                               None if bias is None else bias[b, h])
     return out, lse
 
 
 def fwd_rows(q, k, v, b: int, h: int, rows, dropout_p: float = 0.0, is_causal: bool = False,
-             scale=None, seed: int = 0, offset: int = 0):
+             scale=None, seed: int = 0, offset: int = 0, bias=None):
     """Forward for selected query rows of head (b, h): ``(out [n,E], lse [n])``.
 
     Each row of attention depends only on its own query, so this equals the
@@ -145,12 +162,14 @@ def fwd_rows(q, k, v, b: int, h: int, rows, dropout_p: float = 0.0, is_causal: b
     s = resolve_scale(scale, E)
     valid = valid_mask(Sq, Sk, is_causal, rows=rows)
     mult = dropout_multiplier(dropout_p, seed, offset, B, H, Sq, Sk, b, h, rows=rows)
-    out, lse, _ = head_forward(qh, kh, vh, s, valid, mult)
+    bias = _bias64(bias, B, H, Sq, Sk)
+    out, lse, _ = head_forward(qh, kh, vh, s, valid, mult,
+                               None if bias is None else bias[b, h][rows])
     return out, lse
 
 
 def bwd(dout, q, k, v, dropout_p: float = 0.0, is_causal: bool = False, seed: int = 0,
-        offset: int = 0, scale=None, heads=None):
+        offset: int = 0, scale=None, heads=None, bias=None):
     """Backward on logical [B, H, S, E] inputs: ``(dq, dk, dv)`` in float64.
 
     Computed from (dO, Q, K, V, p, seed, offset, causal, scale) alone; the
@@ -164,8 +183,10 @@ def bwd(dout, q, k, v, dropout_p: float = 0.0, is_causal: bool = False, seed: in
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
     valid = valid_mask(Sq, Sk, is_causal)
+    bias = _bias64(bias, B, H, Sq, Sk)
     for b, h in _heads(B, H, heads):
         mult = dropout_multiplier(dropout_p, seed, offset, B, H, Sq, Sk, b, h)
         dq[b, h], dk[b, h], dv[b, h], _ = head_backward(
-            dout[b, h], q[b, h], k[b, h], v[b, h], s, valid, mult)
+            dout[b, h], q[b, h], k[b, h], v[b, h], s, valid, mult,
+            None if bias is None else bias[b, h])
     return dq, dk, dv

@@ -209,3 +209,87 @@ def test_rows_and_heads_subsets_match_full():
         assert np.array_equal(o_r, out[1, 0, rows]) and np.array_equal(l_r, lse[1, 0, rows])
         out_h, _ = sdpa_ref.fwd(q, k, v, p, causal, None, 9, 11, heads=[(1, 1)])
         assert np.array_equal(out_h[1, 1], out[1, 1]) and np.isnan(out_h[0, 0]).all()
+
+
+# ---- additive bias ----------------------------------------------------------
+
+def test_bias_constant_along_keys_shifts_only_the_lse():
+    # softmax is invariant to adding c_i to every score of row i: O and the
+    # gradients stay, LSE_i moves by c_i.
+    B, H, Sq, Sk, E = 1, 2, 9, 13, 8
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=40)
+    c = _rand((B, H, Sq, 1), 41, 3.0)
+    for causal in (False, True):
+        o0, l0 = sdpa_ref.fwd(q, k, v, 0.0, causal)
+        o1, l1 = sdpa_ref.fwd(q, k, v, 0.0, causal, bias=np.broadcast_to(c, (B, H, Sq, Sk)))
+        assert np.allclose(o1, o0, rtol=1e-12, atol=1e-13)
+        assert np.allclose(l1, l0 + c[..., 0], rtol=1e-12, atol=1e-12)
+        g0 = sdpa_ref.bwd(do, q, k, v, 0.0, causal)
+        g1 = sdpa_ref.bwd(do, q, k, v, 0.0, causal, bias=np.broadcast_to(c, (B, H, Sq, Sk)))
+        for a, b in zip(g0, g1):
+            assert np.allclose(a, b, rtol=1e-11, atol=1e-12)
+
+
+def test_causal_mask_as_a_minus_infinity_bias():
+    # Non-causal attention with -inf above the diagonal is causal attention.
+    B, H, Sq, Sk, E = 2, 1, 11, 11, 8
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=42)
+    bias = np.where(np.arange(Sk)[None, :] > np.arange(Sq)[:, None], -np.inf, 0.0)
+    o_b, l_b = sdpa_ref.fwd(q, k, v, 0.0, False, bias=bias)
+    o_c, l_c = sdpa_ref.fwd(q, k, v, 0.0, True)
+    assert np.allclose(o_b, o_c, rtol=1e-13, atol=1e-14) and np.allclose(l_b, l_c)
+    for a, b in zip(sdpa_ref.bwd(do, q, k, v, 0.0, False, bias=bias),
+                    sdpa_ref.bwd(do, q, k, v, 0.0, True)):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("shape,bshape,causal", [
+    ((1, 2, 48, 64, 32), (1, 2, 48, 64), False),
+    ((2, 2, 40, 40, 16), (1, 2, 40, 40), True),
+    ((1, 3, 32, 56, 16), (32, 56), True),
+])
+def test_bias_against_torch_cpu_float64(shape, bshape, causal):
+    # PyTorch's float attn_mask is an additive term on the scaled scores.
+    B, H, Sq, Sk, E = shape
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=44)
+    bias = _rand(bshape, 45, 2.0)
+    s = 1 / math.sqrt(E)
+    out, _ = sdpa_ref.fwd(q, k, v, 0.0, causal, bias=bias)
+    dq, dk, dv = sdpa_ref.bwd(do, q, k, v, 0.0, causal, bias=bias)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    mask = torch.tensor(np.broadcast_to(bias, (B, H, Sq, Sk)), dtype=torch.float64)
+    if causal:
+        tri = torch.ones(Sq, Sk, dtype=torch.bool).tril()
+        mask = mask.masked_fill(~tri, -math.inf)
+    t_out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=s)
+    t_out.backward(torch.tensor(do, dtype=torch.float64))
+    for a, b in ((out, t_out.detach().numpy()), (dq, tq.grad.numpy()), (dk, tk.grad.numpy()),
+                 (dv, tv.grad.numpy())):
+        assert np.allclose(a, b, rtol=1e-10, atol=1e-11)
+
+
+def test_bias_finite_differences_with_dropout():
+    B, H, Sq, Sk, E = 1, 1, 4, 6, 4
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=46)
+    bias = _rand((Sq, Sk), 47, 1.5)
+    p, seed, off = 0.3, 7, 5
+
+    def loss(qq, kk, vv):
+        out, _ = sdpa_ref.fwd(qq, kk, vv, p, True, None, seed, off, bias=bias)
+        return float((do * out).sum())
+
+    grads = sdpa_ref.bwd(do, q, k, v, p, True, seed, off, bias=bias)
+    step = 1e-6
+    for i, x in enumerate((q, k, v)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xs = [q, k, v]
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += step
+            xm[idx] -= step
+            xs_p, xs_m = list(xs), list(xs)
+            xs_p[i], xs_m[i] = xp, xm
+            fd[idx] = (loss(*xs_p) - loss(*xs_m)) / (2 * step)
+        g = grads[i]
+        err = np.linalg.norm(fd - g) / max(np.linalg.norm(g), 1e-30)
+        assert err <= 1e-6 or np.abs(fd - g).max() < 1e-8, (i, err)
