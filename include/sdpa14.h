@@ -140,12 +140,24 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       are read from it on the device and the host arguments are ignored;
  *       rng_state is ignored.  Both buffers are caller-owned device memory that
  *       must stay valid until the work on `stream` is done.
+ *   bias  (NULL for none)
+ *       Additive attention bias, the relative-position term the forum thread
+ *       "Scaled_dot_product_attention" (opening question) wants SDPA to take
+ *       and the attn_bias support the PyTorch PR "REDO of dropout support for
+ *       mem eff" announces for the memory-efficient kernel: the scores become
+ *       scale * q_i . k_j + bias[b, h, i, j] before masking and softmax, so the
+ *       LSE includes it.  Logical shape [B, H, Sq, Sk], bf16, key stride 1,
+ *       other strides >= 0 and multiples of 4 elements (0 broadcasts that
+ *       dimension), data 8-byte aligned.  -inf entries hide a key; every row
+ *       must keep at least one visible key with a finite score.  Forward and
+ *       backward must be given the same bias; its gradient is not computed.
  */
 typedef struct sdpa_ext {
   int64_t head_offset;
   int64_t heads_total;
   uint64_t* rng_state;
   uint64_t* rng_used;
+  const sdpa_tensor* bias;
 } sdpa_ext;
 
 /* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL. */

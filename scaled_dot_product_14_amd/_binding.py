@@ -49,6 +49,7 @@ class SdpaExt(ctypes.Structure):
         ("heads_total", ctypes.c_int64),
         ("rng_state", ctypes.c_void_p),
         ("rng_used", ctypes.c_void_p),
+        ("bias", ctypes.POINTER(SdpaTensor)),
     ]
 
 
@@ -209,25 +210,35 @@ def _rng_buffer(t, name: str):
     return t.data_ptr()
 
 
-def _ext(head_offset, heads_total, rng_state, rng_used) -> SdpaExt:
+def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None):
+    """The options block and the objects it points into (keep both alive for the call)."""
     e = SdpaExt()
     e.head_offset = int(head_offset)
     e.heads_total = int(heads_total)
     e.rng_state = _rng_buffer(rng_state, "rng_state")
     e.rng_used = _rng_buffer(rng_used, "rng_used")
-    return e
+    keep = None
+    if bias is not None:
+        if bias.dim() > 4:
+            raise ValueError("bias must broadcast to [B, H, Sq, Sk]")
+        full = bias.expand(*shape)  # broadcast dimensions get stride 0
+        desc = describe(full)
+        e.bias = ctypes.pointer(desc)
+        keep = (full, desc)
+    return e, keep
 
 
 def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
                  out=None, lse=None, *, head_offset: int = 0, heads_total: int = 0,
-                 rng_state=None, rng_used=None):
+                 rng_state=None, rng_used=None, bias=None):
     """Forward with options: returns ``(out, lse, seed, offset)``.
 
     ``head_offset`` / ``heads_total`` place the call's heads in a larger problem
     for the dropout stream.  ``rng_state`` and ``rng_used`` (device int64
     tensors of two elements, {seed, offset}) keep the RNG state on the device;
     then ``seed`` and ``offset`` are returned as None and the values the call
-    used land in ``rng_used``.
+    used land in ``rng_used``.  ``bias`` (bf16, broadcastable to
+    [B, H, Sq, Sk], key dimension contiguous) is added to the scaled scores.
     """
     lib = load_library()
     if out is None:
@@ -237,7 +248,8 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
     dq_, dk_, dv_, do_ = describe(q), describe(k), describe(v), describe(out)
-    ext = _ext(head_offset, heads_total, rng_state, rng_used)
+    ext, _keep = _ext(head_offset, heads_total, rng_state, rng_used, bias,
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]))
     seed, offset = ctypes.c_uint64(), ctypes.c_uint64()
     with torch.cuda.device(q.device):
         rc = lib.sdpa_fwd_ext(ctypes.byref(dq_), ctypes.byref(dk_), ctypes.byref(dv_),
@@ -252,7 +264,7 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
 
 def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int = 0,
                  offset: int = 0, scale=None, dq=None, dk=None, dv=None, workspace=None, *,
-                 head_offset: int = 0, heads_total: int = 0, rng_used=None):
+                 head_offset: int = 0, heads_total: int = 0, rng_used=None, bias=None):
     """Backward with options (see ``sdpa_fwd_ext``): returns ``(dq, dk, dv)``.
 
     With ``rng_used`` the kernels read (seed, offset) from that device tensor
@@ -267,7 +279,8 @@ def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, see
         workspace = torch.empty(max(lib.sdpa_bwd_workspace_size(B, H, Sq), 256),
                                 dtype=torch.uint8, device=q.device)
     descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
-    ext = _ext(head_offset, heads_total, None, rng_used)
+    ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]))
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd_ext(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                               float(dropout_p), int(bool(is_causal)), int(seed), int(offset),

@@ -158,7 +158,7 @@ __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], flo
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
 __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                                           unsigned char* lds) {
   using C = BwdCfg<E>;
@@ -195,6 +195,24 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const int nqt = (p.Sq + 31) / 32;
   const int t0 = CAUSAL ? min(kb0 / 32, nqt) : 0;
   const int n_it = (nqt - t0 + 1) / 2;
+
+  // Additive bias at (row q0 + 8*cg + 4*g + u, this lane's key) for register
+  // 4*cg + u, one 2-byte load each (the 32 lanes of a half read 64 contiguous
+  // bytes of one row); step it+1's values are loaded at the start of step it.
+  // Rows past Sq read zeros, keys past Sk are masked.
+  __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
+  if (BIAS)
+    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
+                   (uint32_t)(((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2));
+  uint32_t bias_cur[16], bias_nxt[16];
+  auto load_bias = [&](int t, uint32_t(&dst)[16]) {
+    const int64_t row0 = (int64_t)(t0 + 2 * t + qs) * 32 + 4 * g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      dst[r] = __builtin_amdgcn_raw_buffer_load_b16(
+          br, (uint32_t)(((row0 + 8 * (r >> 2) + (r & 3)) * p.sbias.s + key) * 2), 0, 0);
+  };
+  if (BIAS && n_it > 0) load_bias(0, bias_cur);
 
   // Stage it % 3 of the ring holds query tiles t0 + 2*it and t0 + 2*it + 1.
   uint32_t oq[NLD], odo[NLD];
@@ -288,6 +306,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     const int q0 = (t0 + 2 * it + qs) * 32;
     // Skip tiles past Sq and, when causal, tiles whose rows all precede the keys.
     const bool active = !(q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs));
+    if (BIAS && it + 1 < n_it) load_bias(it + 1, bias_nxt);
     // Every step issues the loads of stage it+2, also past the last stage (those
     // rows lie past Sq and read as zeros into a stage nobody reads again), so
     // the issue points need no branch and every barrier waits the same count.
@@ -305,6 +324,12 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
       for (int cg = 0; cg < 4; ++cg) {
         nd4[cg] = lds_at<f32x4>(dl, (8 * cg + 4 * g) * 4);
         l4[cg] = lds_at<f32x4>(dl, 256 + (8 * cg + 4 * g) * 4);
+      }
+      // A bias enters as L - log2(e) * bias, per element.
+      if (BIAS) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          l4[r >> 2][r & 3] = fmaf(__uint_as_float(bias_cur[r] << 16), -kLog2e, l4[r >> 2][r & 3]);
       }
       f32x16 sacc = zero16(), dpacc;
 #pragma unroll
@@ -363,6 +388,10 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
           if (hf == 1 && (eb == 0 || eb == NEB - 1)) issue_slot(it + 2, eb == 0 ? 3 : 4, 0.f);
         }
     }
+    if (BIAS) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bias_cur[r] = bias_nxt[r];
+    }
     // Stage it+1 must have landed; stage it is free once every wave is past here.
     ring_barrier<C::NPAIR_A>();
   }
@@ -383,7 +412,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
 __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
   using C = BwdCfg<E>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
@@ -414,6 +443,23 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int nkt = (p.Sk + 31) / 32;
   const int kt_end = CAUSAL ? min(nkt, min(q0b + 63, p.Sq - 1) / 32 + 1) : nkt;
   const int n_it = (kt_end + 1) / 2;
+
+  // Additive bias on the row's keys k0 + 8*cg + 4*g + 0..3 (register group cg),
+  // one 8-byte load per group; step it+1's values are loaded at the start of
+  // step it.  Rows past Sq read zeros, keys past Sk are masked.
+  __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
+  if (BIAS)
+    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
+                   (uint32_t)(((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 bias_cur[4], bias_nxt[4];
+  auto load_bias = [&](int t, u32x2(&dst)[4]) {
+    const int64_t base = (int64_t)qrow * p.sbias.s + (2 * t + ks) * 32 + 4 * g;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+      dst[cg] = __builtin_amdgcn_raw_buffer_load_b64(br, (uint32_t)((base + 8 * cg) * 2), 0, 0);
+  };
+  if (BIAS && n_it > 0) load_bias(0, bias_cur);
 
   // Stage it % 3 of the ring holds key tiles 2*it and 2*it + 1.
   uint32_t okk[NLD], ov[NLD];
@@ -510,6 +556,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     const int j = 2 * it + ks;
     const int k0 = j * 32;
     const bool active = !(j >= kt_end || (CAUSAL && k0 > q0 + 31));
+    if (BIAS && it + 1 < n_it) load_bias(it + 1, bias_nxt);
     // Loads of stage it+2 on every step, as in the dK/dV role (past the last
     // stage they fetch rows nobody reads).
     if (!active) issue(it + 2);
@@ -518,6 +565,16 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
       const unsigned char* tk = st + ST_K + ks * TILE_B;
       const unsigned char* tv = st + ST_V + ks * TILE_B;
 
+      // L of the row, minus log2(e) * bias per element when there is a bias.
+      float lb[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        lb[r] = lse2;
+        if (BIAS) {
+          const uint32_t w = bias_cur[r >> 2][(r >> 1) & 1];
+          lb[r] = fmaf(__uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16)), -kLog2e, lse2);
+        }
+      }
       // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
       f32x16 sacc = zero16(), dpacc = dinit;
 #pragma unroll
@@ -547,7 +604,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * cg + u;
-            float x = fmaf(sacc[r], c, -lse2);
+            float x = fmaf(sacc[r], c, -lb[r]);
             if (MASK) x = (8 * cg + u <= lim) ? x : -INFINITY;
             const float ps = fast_exp2(x);
             float dp = dpacc[r];  // dP - D without dropout
@@ -571,6 +628,10 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
           if (hf == 1 && eb == 0) issue_slot(it + 2, 3, 0.f);
         }
     }
+    if (BIAS) {
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) bias_cur[cg] = bias_nxt[cg];
+    }
     ring_barrier<C::NPAIR_B>();
   }
   ring_barrier<0>();  // the trailing loads have landed before the stages are reused
@@ -586,7 +647,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 
 // Workgroup order: per head, dK/dV and dQ blocks alternate, heaviest causal
 // blocks first; all blocks of a head sit on one XCD when the head count allows.
-template <int E, bool CAUSAL, bool DROPOUT>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E>::LDS_B];
   const int bh_count = p.B * p.H;
@@ -611,9 +672,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb)
     rank = slot - m;
   }
   if (dkdv)
-    role_dkdv<E, CAUSAL, DROPOUT>(p, bh, rank, lds);
+    role_dkdv<E, CAUSAL, DROPOUT, BIAS>(p, bh, rank, lds);
   else
-    role_dq<E, CAUSAL, DROPOUT>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
+    role_dq<E, CAUSAL, DROPOUT, BIAS>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
 // -D_i = -rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every
@@ -650,17 +711,27 @@ hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream
                      stream, p);
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
-  if (causal) {
-    if (dropout)
-      hipLaunchKernelGGL((bwd_kernel<E, true, true>), grid, dim3(256), 0, stream, p, nkb, nqb);
+  auto go = [&](auto c, auto d, auto bias) {
+    hipLaunchKernelGGL((bwd_kernel<E, decltype(c)::value, decltype(d)::value,
+                                   decltype(bias)::value>),
+                       grid, dim3(256), 0, stream, p, nkb, nqb);
+  };
+  auto with_bias = [&](auto c, auto d) {
+    if (p.bias != nullptr)
+      go(c, d, Flag<true>{});
     else
-      hipLaunchKernelGGL((bwd_kernel<E, true, false>), grid, dim3(256), 0, stream, p, nkb, nqb);
-  } else {
+      go(c, d, Flag<false>{});
+  };
+  auto with_dropout = [&](auto c) {
     if (dropout)
-      hipLaunchKernelGGL((bwd_kernel<E, false, true>), grid, dim3(256), 0, stream, p, nkb, nqb);
+      with_bias(c, Flag<true>{});
     else
-      hipLaunchKernelGGL((bwd_kernel<E, false, false>), grid, dim3(256), 0, stream, p, nkb, nqb);
-  }
+      with_bias(c, Flag<false>{});
+  };
+  if (causal)
+    with_dropout(Flag<true>{});
+  else
+    with_dropout(Flag<false>{});
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ namespace sdpa14 {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kRescaleSlack = 8.f;  // log2 units the reference max may lag
 
 // Maps a workgroup id to (head, rank); rank 0 is the heaviest query tile.
@@ -62,7 +63,7 @@ __device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& 
   }
 }
 
-template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT>
+template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS>
 __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles) {
   static_assert(E % 64 == 0 && BN % 32 == 0, "tile shape");
   constexpr int NW = NQ * NS;
@@ -119,6 +120,29 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
     qf[es] = __builtin_bit_cast(
         bf16x8, buffer_load16(qr, (uint32_t)(((int64_t)qrow * p.sq.s + es * 16 + 8 * g) * 2)));
 
+  // Additive bias: the lane's query row, keys contiguous.  Register group cg of
+  // key block kb takes the four keys k0 + 32*kb + 8*cg + 4*g + 0..3 in one
+  // 8-byte load; the loads of tile it+1 go out at the start of step it.  Rows
+  // past Sq read zeros (those rows are never stored); keys past Sk are masked.
+  __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
+  uint32_t brow = 0;
+  if (BIAS) {
+    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
+                   (uint32_t)(((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2));
+    brow = (uint32_t)((int64_t)qrow * p.sbias.s * 2);
+  }
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 bias_cur[BN / 32][4], bias_nxt[BN / 32][4];
+  auto load_bias = [&](int t, u32x2(&dst)[BN / 32][4]) {
+    const uint32_t k0b = (uint32_t)((t * NS + ksp) * BN + 4 * g) * 2;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+        dst[kb][cg] = __builtin_amdgcn_raw_buffer_load_b64(br, brow + k0b + (32 * kb + 8 * cg) * 2, 0, 0);
+  };
+  if (BIAS && n_it > 0) load_bias(0, bias_cur);
+
   // K and V rows past kend read as zeros.  Stage it % NSTAGE of the ring holds
   // key rows it*ROWS .. it*ROWS + ROWS-1, loaded straight into LDS.
   const uint32_t kbytes = (uint32_t)(((int64_t)(kend - 1) * p.sk.s + E) * 2);
@@ -165,6 +189,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   float m_run = -INFINITY;  // reference max of scale*log2(e)*S for this row
   float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
   const float c = p.scale_log2;
+  const float cs = BIAS ? 1.f : c;  // factor still to apply to the scores in the softmax
   // Last visible key of this lane's row, for masking (top-left causal; ragged Sk).
   const int key_limit = CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1;
 
@@ -187,6 +212,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
     // Skip tiles past the key range and, when causal, above the diagonal.
     const bool active = (j < n_kt) && (!CAUSAL || k0 <= q0 + 31);
     const bool more = it + NSTAGE - 1 < n_it;
+    if (BIAS && it + 1 < n_it) load_bias(it + 1, bias_nxt);
     if (!active && more) issue(it + NSTAGE - 1);
     if (active) {
       const unsigned char* st = stage(it);
@@ -202,6 +228,19 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
       // The next stage's loads go out behind the first products.
       if (more) issue(it + NSTAGE - 1);
 
+      // With a bias the scores become scale*log2(e)*S + log2(e)*bias here, and
+      // the steps below take them as already scaled.
+      if (BIAS) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t w = bias_cur[kb][r >> 2][(r >> 1) & 1];
+            const float bv = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            s[kb][r] = fmaf(s[kb][r], c, bv * kLog2e);
+          }
+      }
+
       if (k0 + BN - 1 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1)) {
         const int lim = key_limit - k0 - 4 * g;  // key offset past which scores are hidden
 #pragma unroll
@@ -216,7 +255,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-      mx = pair_max(mx) * c;
+      mx = pair_max(mx) * cs;
       // Move the reference max only when it grew by more than the slack; the
       // decision is per row, the skip of the rescale is per wave.
       const bool grow = mx > m_run + kRescaleSlack;
@@ -241,7 +280,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
       for (int ksx = 0; ksx < BN / 16; ++ksx)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], c, -m_use));
+          const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], cs, -m_use));
           rs += pv;
           pb[ksx][i] = (__bf16)pv;
         }
@@ -268,6 +307,12 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
           const int o0 = troff[0][eb] + 16 * ksx * ROW_B, o1 = troff[1][eb] + 16 * ksx * ROW_B;
           oacc[eb] = mfma32x32x16(tr_pair(st, o0, o1), pb[ksx], oacc[eb]);
         }
+    }
+    if (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) bias_cur[kb][cg] = bias_nxt[kb][cg];
     }
     // The next stage must have landed; this one is free once every wave is past here.
     if (NSTAGE == 3 && it + 2 < n_it)
@@ -335,21 +380,27 @@ hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, hipStream
   const int n_qtiles = (p.Sq + BM - 1) / BM;
   const dim3 grid((unsigned)n_qtiles * (unsigned)(p.B * p.H));
   const dim3 block(NQ * NS * 64);
-  if (causal) {
-    if (dropout)
-      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, true, true>), grid, block, 0, stream, p,
-                         n_qtiles);
+  auto go = [&](auto c, auto d, auto bias) {
+    hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, decltype(c)::value, decltype(d)::value,
+                                   decltype(bias)::value>),
+                       grid, block, 0, stream, p, n_qtiles);
+  };
+  auto with_bias = [&](auto c, auto d) {
+    if (p.bias != nullptr)
+      go(c, d, Flag<true>{});
     else
-      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, true, false>), grid, block, 0, stream, p,
-                         n_qtiles);
-  } else {
+      go(c, d, Flag<false>{});
+  };
+  auto with_dropout = [&](auto c) {
     if (dropout)
-      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, false, true>), grid, block, 0, stream, p,
-                         n_qtiles);
+      with_bias(c, Flag<true>{});
     else
-      hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, false, false>), grid, block, 0, stream, p,
-                         n_qtiles);
-  }
+      with_bias(c, Flag<false>{});
+  };
+  if (causal)
+    with_dropout(Flag<true>{});
+  else
+    with_dropout(Flag<false>{});
   return hipGetLastError();
 }
 

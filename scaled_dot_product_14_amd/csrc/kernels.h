@@ -24,6 +24,8 @@ struct FwdParams {
   int B, H, Sq, Sk;
   float scale_log2;  // scale * log2(e)
   DropoutParams drop;
+  const uint16_t* bias;  // additive bias [B, H, Sq, Sk] (bf16 bits, unit key stride), or null
+  Strides sbias;         // its strides (0 for a broadcast dimension)
 };
 
 struct BwdParams {
@@ -42,6 +44,8 @@ struct BwdParams {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   DropoutParams drop;
+  const uint16_t* bias;  // as in FwdParams
+  Strides sbias;
 };
 
 struct MaskParams {

@@ -151,9 +151,30 @@ struct Ext {
   int64_t heads_total = 0;  // the call's H when not sharded
   uint64_t* rng_state = nullptr;
   uint64_t* rng_used = nullptr;
+  const uint16_t* bias = nullptr;
+  Strides sbias{0, 0, 0};
 };
 
-int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, bool forward, Ext* out) {
+int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, Ext* e) {
+  if (t->data == nullptr) return fail(SDPA_ERR_INVALID, "bias data is NULL");
+  if (t->dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "bias dtype must be bf16");
+  if (t->size[0] != B || t->size[1] != H || t->size[2] != Sq || t->size[3] != Sk)
+    return fail(SDPA_ERR_INVALID, "bias must have logical shape [B, H, Sq, Sk] (stride 0 to broadcast)");
+  if (t->stride[3] != 1) return fail(SDPA_ERR_UNSUPPORTED, "bias key stride must be 1");
+  for (int i = 0; i < 3; ++i)
+    if (t->stride[i] < 0 || t->stride[i] % 4 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "bias strides must be >= 0 and multiples of 4 elements");
+  if (reinterpret_cast<uintptr_t>(t->data) % 8 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "bias data is not 8-byte aligned");
+  if (((Sq + 128) * t->stride[2] + Sk) * 2 >= (int64_t(1) << 31))
+    return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice of the bias spans 2 GiB or more");
+  e->bias = static_cast<const uint16_t*>(t->data);
+  e->sbias = Strides{t->stride[0], t->stride[1], t->stride[2]};
+  return SDPA_OK;
+}
+
+int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk, bool forward,
+              Ext* out) {
   Ext e;
   e.heads_total = H;
   if (ext != nullptr) {
@@ -174,6 +195,10 @@ int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, bool forward, Ext* out)
         return fail(SDPA_ERR_UNSUPPORTED, "device RNG buffers must be 8-byte aligned");
     if (e.rng_state != nullptr && e.rng_state == e.rng_used)
       return fail(SDPA_ERR_INVALID, "rng_state and rng_used must be distinct buffers");
+    if (ext->bias != nullptr) {
+      const int rc = check_bias(ext->bias, B, H, Sq, Sk, &e);
+      if (rc) return rc;
+    }
   }
   *out = e;
   return SDPA_OK;
@@ -261,7 +286,7 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   float sc;
   if ((rc = resolve_scale(scale, dq.E, &sc))) return rc;
   Ext e;
-  if ((rc = check_ext(ext, dq.B, dq.H, true, &e))) return rc;
+  if ((rc = check_ext(ext, dq.B, dq.H, dq.S, dk.S, true, &e))) return rc;
   const bool drop = dropout_p > 0.0;
   const uint64_t advance = offset_advance(dq.B, e.heads_total, dq.S, dk.S);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -297,6 +322,8 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   p.Sk = (int)dk.S;
   p.scale_log2 = sc * 1.44269504088896340736f;
   p.drop = make_dropout(dropout_p, s0, o0, e.heads_total, e.head_offset, e.rng_used);
+  p.bias = e.bias;
+  p.sbias = e.sbias;
   const hipError_t err = timed_launch(SDPA_KERNEL_FWD, st, [&] {
     return launch_fwd(p, (int)dq.E, is_causal != 0, drop, tile_choice(), st);
   });
@@ -348,7 +375,7 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   if (workspace_bytes < bwd_workspace_bytes(dqi.B, dqi.H, dqi.S))
     return fail(SDPA_ERR_WORKSPACE, "workspace is smaller than sdpa_bwd_workspace_size()");
   Ext e;
-  if ((rc = check_ext(ext, dqi.B, dqi.H, false, &e))) return rc;
+  if ((rc = check_ext(ext, dqi.B, dqi.H, dqi.S, dki.S, false, &e))) return rc;
 
   BwdParams p;
   p.q = dqi.ptr;
@@ -376,6 +403,8 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   p.scale = sc;
   p.scale_log2 = sc * 1.44269504088896340736f;
   p.drop = make_dropout(dropout_p, seed, offset, e.heads_total, e.head_offset, e.rng_used);
+  p.bias = e.bias;
+  p.sbias = e.sbias;
   const int E = (int)dqi.E;
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -151,3 +151,60 @@ def test_graph_replays_draw_fresh_masks_from_device_state():
         if previous is not None:
             assert not torch.equal(got[0], previous), "replays drew the same mask"
         previous = got[0]
+
+
+def _bias(shape, Sk_pad, seed, scale=2.0, alibi=False):
+    """bf16 bias of logical `shape` (..., Sq, Sk) whose rows are padded to Sk_pad."""
+    Sq, Sk = shape[-2], shape[-1]
+    g = torch.Generator("cpu").manual_seed(seed)
+    full = torch.randn(tuple(shape[:-1]) + (Sk_pad,), generator=g) * scale
+    if alibi:  # a relative-position term: -slope * |i - j|
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Sk_pad)[None, :]
+        full = -0.05 * (i - j).abs().float().expand(tuple(shape[:-1]) + (Sk_pad,))
+    return full.to(torch.bfloat16).to("cuda")[..., :Sk]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,p,bshape,pad,heads", [
+    (2, 3, 200, 200, 64, "BHSE", True, 0.0, "bhqk", 200, None),
+    (1, 2, 130, 250, 128, "BHSE", False, 0.1, "1hqk", 252, None),
+    (2, 2, 256, 256, 64, "BSHE", True, 0.0, "qk-alibi", 256, None),
+    (4, 16, 1000, 1000, 64, "BHSE", True, 0.1, "1hqk", 1000, [(0, 0), (3, 15), (2, 7)]),
+])
+def test_bias_parity(B, H, Sq, Sk, E, layout, causal, p, bshape, pad, heads):
+    say(f"bias {bshape} B{B} H{H} Sq{Sq} Sk{Sk} E{E} {layout} causal={causal} p={p}")
+    q, k, v, do = workloads.draw(B, H, Sq, Sk, E, 16, 1.0, layout, device="cuda")
+    if bshape == "bhqk":
+        bias = _bias((B, H, Sq, Sk), pad, 17)
+    elif bshape == "1hqk":
+        bias = _bias((1, H, Sq, Sk), pad, 18)
+    else:
+        bias = _bias((Sq, Sk), pad, 19, alibi=True)
+    seed, off = 31, 4096
+    sdpa.sdpa_set_rng_state(seed, off)
+    out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, p, causal, bias=bias)
+    dq, dk, dv = sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, p, causal, s, o, bias=bias)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = sdpa_ref.fwd(q, k, v, p, causal, None, seed, off, heads=heads, bias=bias)
+    ref_dq, ref_dk, ref_dv = sdpa_ref.bwd(do, q, k, v, p, causal, seed, off, None, heads=heads,
+                                          bias=bias)
+    sel = (slice(None),) if heads is None else (tuple(b for b, _ in heads), tuple(h for _, h in heads))
+    assert_out(host64(out)[sel], ref_out[sel])
+    assert_lse(lse.cpu().double().numpy()[sel], ref_lse[sel])
+    assert_grads([("dq", host64(dq)[sel], ref_dq[sel]), ("dk", host64(dk)[sel], ref_dk[sel]),
+                  ("dv", host64(dv)[sel], ref_dv[sel])])
+
+
+def test_zero_bias_equals_no_bias():
+    q, k, v, do = workloads.draw(2, 2, 192, 192, 64, 20, 1.0, "BHSE", device="cuda")
+    zero = torch.zeros((192, 192), dtype=torch.bfloat16, device="cuda")
+    o1, l1, s, f = sdpa.sdpa_fwd_ext(q, k, v, 0.0, True, bias=zero)
+    g1 = sdpa.sdpa_bwd_ext(do, q, k, v, o1, l1, 0.0, True, s, f, bias=zero)
+    o2, l2, s, f = sdpa.sdpa_fwd(q, k, v, 0.0, True)
+    g2 = sdpa.sdpa_bwd(do, q, k, v, o2, l2, 0.0, True, s, f)
+    torch.cuda.synchronize()
+    # Same math up to the order of one multiply-add, so within rounding of bf16 outputs.
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-5
+    for a, b in zip(g1, g2):
+        assert (a.float() - b.float()).abs().max().item() <= 2e-2

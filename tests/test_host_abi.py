@@ -138,10 +138,24 @@ def test_backward_checks_workspace(lib, kw, needle):
     assert bnd.sdpa_get_rng_state() == (7, 8)
 
 
-def _ext(head_offset=0, heads_total=0, rng_state=None, rng_used=None):
+_BIAS_KEEP = []
+
+
+def _ext(head_offset=0, heads_total=0, rng_state=None, rng_used=None, bias=None):
     e = bnd.SdpaExt()
     e.head_offset, e.heads_total, e.rng_state, e.rng_used = head_offset, heads_total, rng_state, rng_used
+    if bias is not None:
+        _BIAS_KEEP.append(bias)
+        e.bias = ctypes.pointer(bias)
     return e
+
+
+def _bias(size=(1, 2, 128, 128), stride=(0, 128 * 128, 128, 1), data=FAKE, dtype=0):
+    d = bnd.SdpaTensor()
+    d.data, d.dtype = data, dtype
+    for i in range(4):
+        d.size[i], d.stride[i] = size[i], stride[i]
+    return d
 
 
 @pytest.mark.parametrize("ext,code,needle", [
@@ -153,6 +167,14 @@ def _ext(head_offset=0, heads_total=0, rng_state=None, rng_used=None):
     (_ext(rng_used=FAKE), bnd.SDPA_ERR_INVALID, "together"),
     (_ext(rng_state=FAKE, rng_used=FAKE), bnd.SDPA_ERR_INVALID, "distinct"),
     (_ext(rng_state=FAKE + 4, rng_used=FAKE + 64), bnd.SDPA_ERR_UNSUPPORTED, "aligned"),
+    (_ext(bias=_bias(data=0)), bnd.SDPA_ERR_INVALID, "bias data"),
+    (_ext(bias=_bias(dtype=1)), bnd.SDPA_ERR_UNSUPPORTED, "bias dtype"),
+    (_ext(bias=_bias(size=(1, 2, 128, 64))), bnd.SDPA_ERR_INVALID, "shape"),
+    (_ext(bias=_bias(stride=(0, 0, 1, 128))), bnd.SDPA_ERR_UNSUPPORTED, "key stride"),
+    (_ext(bias=_bias(stride=(0, 0, 130, 1))), bnd.SDPA_ERR_UNSUPPORTED, "multiples of 4"),
+    (_ext(bias=_bias(stride=(0, -128, 128, 1))), bnd.SDPA_ERR_UNSUPPORTED, ">= 0"),
+    (_ext(bias=_bias(data=FAKE + 2)), bnd.SDPA_ERR_UNSUPPORTED, "8-byte"),
+    (_ext(bias=_bias(stride=(0, 0, 1 << 24, 1))), bnd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
 ])
 def test_forward_ext_rejects_bad_options(lib, ext, code, needle):
     bnd.sdpa_set_rng_state(31, 41)
