@@ -16,8 +16,9 @@ Prints ONE JSON line:
   cpu_baseline  the fp64 CPU oracle on the host cores (a reported baseline)
 
 Options: --steps K --warmup W --gpus N (N must be 1), --no-cpu-baseline,
---workload NAME, --shape B,H,Sq,Sk,E,causal[,p], --copy-bytes N (time a plain device copy of N bytes instead,
-for calibrating hardware byte counters).
+--workload NAME, --shape B,H,Sq,Sk,E,causal[,p], --bias {none,qk,bhqk} (an additive bias through the
+extended calls), --copy-bytes N (time a plain device copy of N bytes instead, for calibrating
+hardware byte counters).
 """
 
 from __future__ import annotations
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--bias", choices=("none", "qk", "bhqk"), default="none",
+                    help="add an additive bf16 bias: [Sq, Sk] broadcast over batch and heads, "
+                         "or a full [B, H, Sq, Sk] (drawn N(0, 4)); timed through the extended calls")
     ap.add_argument("--shape", default="",
                     help="B,H,Sq,Sk,E,causal[,p] instead of a named workload (exploration)")
     return ap.parse_args()
@@ -193,15 +197,28 @@ def main():
                      device="cuda")
     sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset)
     state = {}
+    bias = None
+    if args.bias != "none":
+        gb = torch.Generator("cpu").manual_seed(8)
+        bshape = (w.Sq, w.Sk) if args.bias == "qk" else (w.B, w.H, w.Sq, w.Sk)
+        bias = (torch.randn(bshape, generator=gb) * 2.0).to(torch.bfloat16).to("cuda")
 
     def fwd():
-        _, _, s, o = sdpa.sdpa_fwd(q, k, v, w.dropout_p, w.causal, None, out=out, lse=lse)
+        if bias is None:
+            _, _, s, o = sdpa.sdpa_fwd(q, k, v, w.dropout_p, w.causal, None, out=out, lse=lse)
+        else:
+            _, _, s, o = sdpa.sdpa_fwd_ext(q, k, v, w.dropout_p, w.causal, None, out=out,
+                                           lse=lse, bias=bias)
         state["so"] = (s, o)
 
     def bwd():
         s, o = state["so"]
-        sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq, dk=dk,
-                      dv=dv, workspace=ws)
+        if bias is None:
+            sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
+                          dk=dk, dv=dv, workspace=ws)
+        else:
+            sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
+                              dk=dk, dv=dv, workspace=ws, bias=bias)
 
     def step():
         fwd()
@@ -262,7 +279,7 @@ def main():
     dk_ = kern[dominant]
     roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
-            "traffic": measured_traffic(w.name, dominant)}
+            "traffic": measured_traffic(w.name, dominant) if bias is None else None}
 
     result = {
         "metric": METRIC,
@@ -279,7 +296,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "E": w.E,
                    "layout": w.layout, "causal": w.causal, "dropout_p": w.dropout_p,
-                   "cache": "warm (same buffers every step)"},
+                   "bias": args.bias, "cache": "warm (same buffers every step)"},
         "timing": "graph replay of the captured step (eager_ms_per_step: the same step "
                   "issued from Python each time)",
         "eager_ms_per_step": ms_eager,

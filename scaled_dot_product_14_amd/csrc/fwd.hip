@@ -189,7 +189,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   float m_run = -INFINITY;  // reference max of scale*log2(e)*S for this row
   float l_run = 0.f;        // this lane's share of the row sum, relative to m_run
   const float c = p.scale_log2;
-  const float cs = BIAS ? 1.f : c;  // factor still to apply to the scores in the softmax
+  const float inv_scale = kLog2e / c;  // 1 / scale, for the bias
   // Last visible key of this lane's row, for masking (top-left causal; ragged Sk).
   const int key_limit = CAUSAL ? min(qrow, p.Sk - 1) : p.Sk - 1;
 
@@ -216,30 +216,26 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
     if (!active && more) issue(it + NSTAGE - 1);
     if (active) {
       const unsigned char* st = stage(it);
-      // S^T for BN keys x 32 queries.
+      // S^T for BN keys x 32 queries.  A bias enters as the accumulator's
+      // starting value bias / scale, so the products leave S + bias / scale and
+      // the softmax below scales by scale * log2(e) as without one.
       f32x16 s[BN / 32];
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb) {
         s[kb] = zero16();
+        if (BIAS) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t w = bias_cur[kb][r >> 2][(r >> 1) & 1];
+            s[kb][r] = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16)) * inv_scale;
+          }
+        }
 #pragma unroll
         for (int es = 0; es < NES; ++es)
           s[kb] = mfma32x32x16(lds_at<bf16x8>(st, aoff[es] + kb * 32 * ROW_B), qf[es], s[kb]);
       }
       // The next stage's loads go out behind the first products.
       if (more) issue(it + NSTAGE - 1);
-
-      // With a bias the scores become scale*log2(e)*S + log2(e)*bias here, and
-      // the steps below take them as already scaled.
-      if (BIAS) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t w = bias_cur[kb][r >> 2][(r >> 1) & 1];
-            const float bv = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16));
-            s[kb][r] = fmaf(s[kb][r], c, bv * kLog2e);
-          }
-      }
 
       if (k0 + BN - 1 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1)) {
         const int lim = key_limit - k0 - 4 * g;  // key offset past which scores are hidden
@@ -255,7 +251,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-      mx = pair_max(mx) * cs;
+      mx = pair_max(mx) * c;
       // Move the reference max only when it grew by more than the slack; the
       // decision is per row, the skip of the rescale is per wave.
       const bool grow = mx > m_run + kRescaleSlack;
@@ -280,7 +276,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
       for (int ksx = 0; ksx < BN / 16; ++ksx)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], cs, -m_use));
+          const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], c, -m_use));
           rs += pv;
           pb[ksx][i] = (__bf16)pv;
         }
