@@ -33,8 +33,9 @@
  * Tensors: logical shape [B, H, S, E] with arbitrary element strides for the
  * first three dimensions and unit stride for E.  This covers both stride orders
  * of the nvFuser test: BHSE (memory [b, h, s, e]) and BSHE (memory [b, s, h, e]).
- * Supported now: dtype bf16, E in {64, 128}; data pointers 16-byte aligned and
- * the first three strides multiples of 8 elements.
+ * Supported now: dtype bf16 or fp16 (IEEE half; one per call), E in {64, 128};
+ * data pointers 16-byte aligned and the first three strides multiples of 8
+ * elements.
  *
  * Memory: every buffer is owned by the caller and lives on the current HIP
  * device; the library never allocates or frees device memory.  All work is
@@ -67,7 +68,10 @@ typedef enum sdpa_status {
   SDPA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } sdpa_status;
 
-typedef enum sdpa_dtype { SDPA_BF16 = 0 } sdpa_dtype;
+/* 16-bit element formats; all tensors of one call share one format (the
+ * bias too).  Arithmetic is the same for both: 16-bit products into fp32
+ * MFMA accumulators, fp32 softmax. */
+typedef enum sdpa_dtype { SDPA_BF16 = 0, SDPA_F16 = 1 } sdpa_dtype;
 
 /* A strided device tensor with logical shape [B, H, S, E]. */
 typedef struct sdpa_tensor {
@@ -160,7 +164,10 @@ typedef struct sdpa_ext {
   const sdpa_tensor* bias;
 } sdpa_ext;
 
-/* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL. */
+/* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL.
+ * sdpa_fwd_ext also accepts lse == NULL: an inference-only forward (the
+ * inference node of nvFuser issue 2278) that writes no log-sum-exp, so no
+ * backward can follow it. */
 int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
                  double dropout_p, int is_causal, double scale,
                  const sdpa_tensor* out, float* lse,

@@ -22,6 +22,7 @@ SDPA_ERR_UNSUPPORTED = 2
 SDPA_ERR_WORKSPACE = 3
 SDPA_ERR_HIP = 4
 SDPA_BF16 = 0
+SDPA_F16 = 1
 
 KERNEL_FWD = 0
 KERNEL_BWD = 1
@@ -128,7 +129,7 @@ def describe(t: torch.Tensor) -> SdpaTensor:
         raise ValueError(f"expected a 4-D [B, H, S, E] tensor, got shape {tuple(t.shape)}")
     d = SdpaTensor()
     d.data = t.data_ptr()
-    d.dtype = SDPA_BF16 if t.dtype == torch.bfloat16 else -1
+    d.dtype = {torch.bfloat16: SDPA_BF16, torch.float16: SDPA_F16}.get(t.dtype, -1)
     for i in range(4):
         d.size[i] = t.shape[i]
         d.stride[i] = t.stride(i)
@@ -230,7 +231,7 @@ def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None):
 
 def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
                  out=None, lse=None, *, head_offset: int = 0, heads_total: int = 0,
-                 rng_state=None, rng_used=None, bias=None):
+                 rng_state=None, rng_used=None, bias=None, need_lse: bool = True):
     """Forward with options: returns ``(out, lse, seed, offset)``.
 
     ``head_offset`` / ``heads_total`` place the call's heads in a larger problem
@@ -239,14 +240,19 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
     then ``seed`` and ``offset`` are returned as None and the values the call
     used land in ``rng_used``.  ``bias`` (bf16, broadcastable to
     [B, H, Sq, Sk], key dimension contiguous) is added to the scaled scores.
+    ``need_lse=False`` runs the inference-only forward: no log-sum-exp is
+    written and ``lse`` is returned as None.
     """
     lib = load_library()
     if out is None:
         out = torch.empty_like(q)
-    if lse is None:
+    if lse is None and need_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+    if need_lse and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                     or tuple(lse.shape) != tuple(q.shape[:3])):
         raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    if not need_lse:
+        lse = None
     dq_, dk_, dv_, do_ = describe(q), describe(k), describe(v), describe(out)
     ext, _keep = _ext(head_offset, heads_total, rng_state, rng_used, bias,
                       (q.shape[0], q.shape[1], q.shape[2], k.shape[2]))
@@ -254,7 +260,8 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
     with torch.cuda.device(q.device):
         rc = lib.sdpa_fwd_ext(ctypes.byref(dq_), ctypes.byref(dk_), ctypes.byref(dv_),
                               float(dropout_p), int(bool(is_causal)), _scale_arg(scale),
-                              ctypes.byref(do_), lse.data_ptr(), ctypes.byref(seed),
+                              ctypes.byref(do_), None if lse is None else lse.data_ptr(),
+                              ctypes.byref(seed),
                               ctypes.byref(offset), ctypes.byref(ext), _stream(q.device))
     _check(rc)
     if rng_state is not None:

@@ -134,7 +134,7 @@ __device__ __forceinline__ void exchange_put(const f32x16 (&acc)[E / 32], float*
   }
 }
 
-template <int E>
+template <int E, bool F16>
 __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], float mul,
                                                 uint16_t* dst, int64_t stride, int row0,
                                                 int limit, const float* red, int partner_slot,
@@ -151,14 +151,14 @@ __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], flo
     for (int cg = 0; cg < 4; ++cg) {
       const f32x4 o = buf[(i * 4 + cg) * 64 + lane];
       *reinterpret_cast<uint2*>(dst + (int64_t)row * stride + eb * 32 + 8 * cg + 4 * g) =
-          pack_bf16x4((acc[eb][4 * cg + 0] + o[0]) * mul, (acc[eb][4 * cg + 1] + o[1]) * mul,
+          pack16x4<F16>((acc[eb][4 * cg + 0] + o[0]) * mul, (acc[eb][4 * cg + 1] + o[1]) * mul,
                       (acc[eb][4 * cg + 2] + o[2]) * mul, (acc[eb][4 * cg + 3] + o[3]) * mul);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                                           unsigned char* lds) {
   using C = BwdCfg<E>;
@@ -329,15 +329,15 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
       if (BIAS) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          l4[r >> 2][r & 3] = fmaf(__uint_as_float(bias_cur[r] << 16), -kLog2e, l4[r >> 2][r & 3]);
+          l4[r >> 2][r & 3] = fmaf(from16<F16>(bias_cur[r]), -kLog2e, l4[r >> 2][r & 3]);
       }
       f32x16 sacc = zero16(), dpacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) dpacc[r] = DROPOUT ? 0.f : nd4[r >> 2][r & 3];
 #pragma unroll
       for (int es = 0; es < NES; ++es) {
-        sacc = mfma32x32x16(lds_at<bf16x8>(tq, aoff[es]), kf[es], sacc);
-        dpacc = mfma32x32x16(lds_at<bf16x8>(tdo, aoff[es]), vf[es], dpacc);
+        sacc = mfma16<F16>(lds_at<bf16x8>(tq, aoff[es]), kf[es], sacc);
+        dpacc = mfma16<F16>(lds_at<bf16x8>(tdo, aoff[es]), vf[es], dpacc);
       }
       issue_slot(it + 2, 0, 0.f);
 
@@ -368,8 +368,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
               pd = keep ? ps * drop.keep_scale : 0.f;
               dp = (keep ? dp * drop.keep_scale : 0.f) + nd4[cg][u];
             }
-            pb[r >> 3][r & 7] = (__bf16)pd;
-            dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
+            pb[r >> 3][r & 7] = to16<F16>(pd);
+            dsb[r >> 3][r & 7] = to16<F16>(ps * dp);
             if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
           }
         }
@@ -383,8 +383,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
-          dva[eb] = mfma32x32x16(tr_pair(tdo, o0, o1), pb[hf], dva[eb]);
-          dka[eb] = mfma32x32x16(tr_pair(tq, o0, o1), dsb[hf], dka[eb]);
+          dva[eb] = mfma16<F16>(tr_pair(tdo, o0, o1), pb[hf], dva[eb]);
+          dka[eb] = mfma16<F16>(tr_pair(tq, o0, o1), dsb[hf], dka[eb]);
           if (hf == 1 && (eb == 0 || eb == NEB - 1)) issue_slot(it + 2, eb == 0 ? 3 : 4, 0.f);
         }
     }
@@ -407,12 +407,12 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   uint16_t* dvp = p.dv + b * p.sdv.b + h * p.sdv.h;
   uint16_t* dkp = p.dk + b * p.sdk.b + h * p.sdk.h;
   const int partner = 4 * sb + 2 * (1 - qs);
-  exchange_finish<E>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, red, partner + 0, upper, lane);
-  exchange_finish<E>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, red, partner + 1, upper, lane);
+  exchange_finish<E, F16>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, red, partner + 0, upper, lane);
+  exchange_finish<E, F16>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, red, partner + 1, upper, lane);
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
   using C = BwdCfg<E>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
@@ -572,15 +572,15 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
         lb[r] = lse2;
         if (BIAS) {
           const uint32_t w = bias_cur[r >> 2][(r >> 1) & 1];
-          lb[r] = fmaf(__uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16)), -kLog2e, lse2);
+          lb[r] = fmaf(from16<F16>((r & 1) ? (w >> 16) : w), -kLog2e, lse2);
         }
       }
       // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
       f32x16 sacc = zero16(), dpacc = dinit;
 #pragma unroll
       for (int es = 0; es < NES; ++es) {
-        sacc = mfma32x32x16(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
-        dpacc = mfma32x32x16(lds_at<bf16x8>(tv, aoff[es]), dof[es], dpacc);
+        sacc = mfma16<F16>(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
+        dpacc = mfma16<F16>(lds_at<bf16x8>(tv, aoff[es]), dof[es], dpacc);
       }
       issue_slot(it + 2, 0, 0.f);
 
@@ -609,7 +609,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
             const float ps = fast_exp2(x);
             float dp = dpacc[r];  // dP - D without dropout
             if (DROPOUT) dp = (((kbits >> u) & 1) ? dp * drop.keep_scale : 0.f) + ndsum;
-            dsb[r >> 3][r & 7] = (__bf16)(ps * dp);
+            dsb[r >> 3][r & 7] = to16<F16>(ps * dp);
             if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
           }
         }
@@ -624,7 +624,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
-          dqa[eb] = mfma32x32x16(tr_pair(tk, o0, o1), dsb[hf], dqa[eb]);
+          dqa[eb] = mfma16<F16>(tr_pair(tk, o0, o1), dsb[hf], dqa[eb]);
           if (hf == 1 && eb == 0) issue_slot(it + 2, 3, 0.f);
         }
     }
@@ -642,12 +642,12 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   exchange_put<E>(dqa, red, 2 * qsb + ks, upper, lane);
   ring_barrier<0>();
   uint16_t* dqp = p.dq + b * p.sdq.b + h * p.sdq.h;
-  exchange_finish<E>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, red, 2 * qsb + (1 - ks), upper, lane);
+  exchange_finish<E, F16>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, red, 2 * qsb + (1 - ks), upper, lane);
 }
 
 // Workgroup order: per head, dK/dV and dQ blocks alternate, heaviest causal
 // blocks first; all blocks of a head sit on one XCD when the head count allows.
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E>::LDS_B];
   const int bh_count = p.B * p.H;
@@ -672,15 +672,15 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb)
     rank = slot - m;
   }
   if (dkdv)
-    role_dkdv<E, CAUSAL, DROPOUT, BIAS>(p, bh, rank, lds);
+    role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16>(p, bh, rank, lds);
   else
-    role_dq<E, CAUSAL, DROPOUT, BIAS>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
+    role_dq<E, CAUSAL, DROPOUT, BIAS, F16>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
 // -D_i = -rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every
 // row, in two planes of B*H*Sq floats.  CPR lanes share a row; each loads one
 // 16-byte chunk of dO and of O.
-template <int E>
+template <int E, bool F16>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int CPR = E / 8, RPB = 256 / CPR;
   const int tid = threadIdx.x;
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     const int64_t b = bh / p.H, h = bh - (bh / p.H) * p.H;
     const bf16x8 x = load_bf16x8(p.dout + b * p.sdo.b + h * p.sdo.h + i * p.sdo.s + col * 8);
     const bf16x8 y = load_bf16x8(p.o + b * p.so.b + h * p.so.h + i * p.so.s + col * 8);
-    d = dot8_bf16(x, y, 0.f);
+    d = dot8_16<F16>(x, y, 0.f);
   }
   d = group_sum<CPR>(d);
   if (row < rows && col == 0) {
@@ -703,17 +703,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   }
 }
 
-template <int E>
+template <int E, bool F16>
 hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
   constexpr int RPB = 256 / (E / 8);
   const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  hipLaunchKernelGGL((bwd_prep_kernel<E>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, p);
+  hipLaunchKernelGGL((bwd_prep_kernel<E, F16>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                     dim3(256), 0, stream, p);
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
   auto go = [&](auto c, auto d, auto bias) {
     hipLaunchKernelGGL((bwd_kernel<E, decltype(c)::value, decltype(d)::value,
-                                   decltype(bias)::value>),
+                                   decltype(bias)::value, F16>),
                        grid, dim3(256), 0, stream, p, nkb, nqb);
   };
   auto with_bias = [&](auto c, auto d) {
@@ -742,9 +742,13 @@ size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   return (raw + 255u) & ~(size_t)255u;
 }
 
-hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream) {
-  return E == 64 ? launch_bwd_t<64>(p, causal, dropout, stream)
-                 : launch_bwd_t<128>(p, causal, dropout, stream);
+hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, bool f16,
+                      hipStream_t stream) {
+  if (f16)
+    return E == 64 ? launch_bwd_t<64, true>(p, causal, dropout, stream)
+                   : launch_bwd_t<128, true>(p, causal, dropout, stream);
+  return E == 64 ? launch_bwd_t<64, false>(p, causal, dropout, stream)
+                 : launch_bwd_t<128, false>(p, causal, dropout, stream);
 }
 
 }  // namespace sdpa14

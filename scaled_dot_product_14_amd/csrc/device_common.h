@@ -1,4 +1,4 @@
-// Device helpers for the gfx950 (CDNA4) attention kernels: bf16 MFMA tiles,
+// Device helpers for the gfx950 (CDNA4) attention kernels: bf16 / fp16 MFMA tiles,
 // LDS transposed reads and cross-half wavefront exchange.
 //
 // Lane layouts used throughout (wave64, checked on gfx950):
@@ -114,6 +114,64 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
   v[2] = (__bf16)c;
   v[3] = (__bf16)d;
   return __builtin_bit_cast(uint2, v);
+}
+
+// ---- 16-bit element formats ----------------------------------------------
+// Fragments travel as bf16x8 / bf16x4 bit containers whatever the format; the
+// F16 flag picks IEEE half instead of bfloat16 where values are multiplied or
+// converted.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// float -> 16-bit value (round to nearest even), as a bit container.
+template <bool F16>
+__device__ __forceinline__ __bf16 to16(float x) {
+  if constexpr (F16)
+    return __builtin_bit_cast(__bf16, static_cast<_Float16>(x));
+  else
+    return static_cast<__bf16>(x);
+}
+
+// The 16-bit value in the low half of `bits` -> float.
+template <bool F16>
+__device__ __forceinline__ float from16(uint32_t bits) {
+  if constexpr (F16)
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+  else
+    return __uint_as_float(bits << 16);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint2 pack16x4(float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = to16<F16>(a);
+  v[1] = to16<F16>(b);
+  v[2] = to16<F16>(c);
+  v[3] = to16<F16>(d);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// acc + sum_i x_i * y_i over 8 16-bit values, fp32 accumulation.
+template <bool F16>
+__device__ __forceinline__ float dot8_16(const bf16x8& x, const bf16x8& y, float acc) {
+  if constexpr (F16) {
+    const f16x8 a = __builtin_bit_cast(f16x8, x), b = __builtin_bit_cast(f16x8, y);
+#pragma unroll
+    for (int i = 0; i < 8; i += 2)
+      acc = __builtin_amdgcn_fdot2(f16x2{a[i], a[i + 1]}, f16x2{b[i], b[i + 1]}, acc, false);
+    return acc;
+  } else {
+    return dot8_bf16(x, y, acc);
+  }
 }
 
 // Within-row lane permutations (DPP): xor 1, xor 2 (quad_perm), and the

@@ -63,7 +63,7 @@ __device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& 
   }
 }
 
-template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS>
+template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles) {
   static_assert(E % 64 == 0 && BN % 32 == 0, "tile shape");
   constexpr int NW = NQ * NS;
@@ -227,12 +227,12 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const uint32_t w = bias_cur[kb][r >> 2][(r >> 1) & 1];
-            s[kb][r] = __uint_as_float((r & 1) ? (w & 0xFFFF0000u) : (w << 16)) * inv_scale;
+            s[kb][r] = from16<F16>((r & 1) ? (w >> 16) : w) * inv_scale;
           }
         }
 #pragma unroll
         for (int es = 0; es < NES; ++es)
-          s[kb] = mfma32x32x16(lds_at<bf16x8>(st, aoff[es] + kb * 32 * ROW_B), qf[es], s[kb]);
+          s[kb] = mfma16<F16>(lds_at<bf16x8>(st, aoff[es] + kb * 32 * ROW_B), qf[es], s[kb]);
       }
       // The next stage's loads go out behind the first products.
       if (more) issue(it + NSTAGE - 1);
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
         for (int i = 0; i < 8; ++i) {
           const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], c, -m_use));
           rs += pv;
-          pb[ksx][i] = (__bf16)pv;
+          pb[ksx][i] = to16<F16>(pv);
         }
       l_run += rs;
 
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 #pragma unroll
         for (int ksx = 0; ksx < BN / 16; ++ksx) {
           const int o0 = troff[0][eb] + 16 * ksx * ROW_B, o1 = troff[1][eb] + 16 * ksx * ROW_B;
-          oacc[eb] = mfma32x32x16(tr_pair(st, o0, o1), pb[ksx], oacc[eb]);
+          oacc[eb] = mfma16<F16>(tr_pair(st, o0, o1), pb[ksx], oacc[eb]);
         }
     }
     if (BIAS) {
@@ -363,23 +363,30 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
       for (int cg = 0; cg < 4; ++cg) {
         const int e = eb * 32 + 8 * cg + 4 * g;
         *reinterpret_cast<uint2*>(op + e) =
-            pack_bf16x4(oacc[eb][4 * cg + 0] * inv, oacc[eb][4 * cg + 1] * inv,
+            pack16x4<F16>(oacc[eb][4 * cg + 0] * inv, oacc[eb][4 * cg + 1] * inv,
                         oacc[eb][4 * cg + 2] * inv, oacc[eb][4 * cg + 3] * inv);
       }
-    if (g == 0) p.lse[(int64_t)bh * p.Sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * p.Sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
 template <int E, int NQ, int NS, int BN>
-hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, hipStream_t stream) {
+hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, bool f16,
+                        hipStream_t stream) {
   constexpr int BM = NQ * 32;
   const int n_qtiles = (p.Sq + BM - 1) / BM;
   const dim3 grid((unsigned)n_qtiles * (unsigned)(p.B * p.H));
   const dim3 block(NQ * NS * 64);
-  auto go = [&](auto c, auto d, auto bias) {
+  auto go2 = [&](auto c, auto d, auto bias, auto half) {
     hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, decltype(c)::value, decltype(d)::value,
-                                   decltype(bias)::value>),
+                                   decltype(bias)::value, decltype(half)::value>),
                        grid, block, 0, stream, p, n_qtiles);
+  };
+  auto go = [&](auto c, auto d, auto bias) {
+    if (f16)
+      go2(c, d, bias, Flag<true>{});
+    else
+      go2(c, d, bias, Flag<false>{});
   };
   auto with_bias = [&](auto c, auto d) {
     if (p.bias != nullptr)
@@ -402,7 +409,7 @@ hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, hipStream
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
+hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool f16,
                       const TileChoice& tiles, hipStream_t stream) {
   // Shape: 4 query sub-tiles sharing each key tile when there are enough
   // 128-row tiles to give every compute unit two workgroups; otherwise two
@@ -413,14 +420,14 @@ hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
     shape = (wg4 >= 512) ? 1 : 2;
   }
   if (E == 64) {
-    if (shape == 1) return launch_fwd_t<64, 4, 1, 64>(p, causal, dropout, stream);
-    if (shape == 2) return launch_fwd_t<64, 2, 2, 64>(p, causal, dropout, stream);
-    return launch_fwd_t<64, 1, 4, 64>(p, causal, dropout, stream);
+    if (shape == 1) return launch_fwd_t<64, 4, 1, 64>(p, causal, dropout, f16, stream);
+    if (shape == 2) return launch_fwd_t<64, 2, 2, 64>(p, causal, dropout, f16, stream);
+    return launch_fwd_t<64, 1, 4, 64>(p, causal, dropout, f16, stream);
   }
   // One query sub-tile with four key shares needs more registers than head dim
   // 128 leaves; it falls back to two by two.
-  if (shape == 1) return launch_fwd_t<128, 4, 1, 64>(p, causal, dropout, stream);
-  return launch_fwd_t<128, 2, 2, 64>(p, causal, dropout, stream);
+  if (shape == 1) return launch_fwd_t<128, 4, 1, 64>(p, causal, dropout, f16, stream);
+  return launch_fwd_t<128, 2, 2, 64>(p, causal, dropout, f16, stream);
 }
 
 }  // namespace sdpa14

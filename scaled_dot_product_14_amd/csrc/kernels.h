@@ -19,7 +19,7 @@ struct FwdParams {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  float* lse;  // contiguous [B, H, Sq]
+  float* lse;  // contiguous [B, H, Sq], or null (inference: not written)
   Strides sq, sk, sv, so;
   int B, H, Sq, Sk;
   float scale_log2;  // scale * log2(e)
@@ -60,11 +60,13 @@ struct TileChoice {
                   // shares, 3 = 1 sub-tile x 4 key shares (32 query rows per sub-tile)
 };
 
-hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout,
+// f16: the 16-bit tensors are IEEE half instead of bfloat16.
+hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool f16,
                       const TileChoice& tiles, hipStream_t stream);
 // Backward: a row pass filling p.dl, then the main kernel.  p.dl must hold
 // bwd_workspace_bytes(B, H, Sq) bytes.
-hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, bool f16,
+                      hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream);
 // One thread: used[0..1] = state[0..1], then state[1] += advance.

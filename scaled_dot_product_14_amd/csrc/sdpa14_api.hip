@@ -45,6 +45,7 @@ struct Desc {
   const uint16_t* ptr;
   int64_t B, H, S, E;
   Strides st;
+  int dtype;
 };
 
 // Validates one tensor descriptor and resolves its strides.  Strides of
@@ -56,8 +57,9 @@ int check_tensor(const sdpa_tensor* t, const char* name, Desc* d) {
     if (t->size[i] < 1)
       return fail(SDPA_ERR_INVALID, "%s: size[%d] = %lld must be >= 1", name, i,
                   (long long)t->size[i]);
-  if (t->dtype != SDPA_BF16)
-    return fail(SDPA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (bf16 only)", name, t->dtype);
+  if (t->dtype != SDPA_BF16 && t->dtype != SDPA_F16)
+    return fail(SDPA_ERR_UNSUPPORTED, "%s: dtype %d is not supported (bf16 or f16)", name,
+                t->dtype);
   if (t->stride[3] != 1 && t->size[3] > 1)
     return fail(SDPA_ERR_UNSUPPORTED, "%s: stride of the head dim is %lld, must be 1", name,
                 (long long)t->stride[3]);
@@ -82,6 +84,7 @@ int check_tensor(const sdpa_tensor* t, const char* name, Desc* d) {
   d->S = t->size[2];
   d->E = t->size[3];
   d->st = Strides{st[0], st[1], st[2]};
+  d->dtype = t->dtype;
   return SDPA_OK;
 }
 
@@ -155,9 +158,11 @@ struct Ext {
   Strides sbias{0, 0, 0};
 };
 
-int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, Ext* e) {
+int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int dtype,
+               Ext* e) {
   if (t->data == nullptr) return fail(SDPA_ERR_INVALID, "bias data is NULL");
-  if (t->dtype != SDPA_BF16) return fail(SDPA_ERR_UNSUPPORTED, "bias dtype must be bf16");
+  if (t->dtype != dtype)
+    return fail(SDPA_ERR_UNSUPPORTED, "bias dtype must be the dtype of q");
   if (t->size[0] != B || t->size[1] != H || t->size[2] != Sq || t->size[3] != Sk)
     return fail(SDPA_ERR_INVALID, "bias must have logical shape [B, H, Sq, Sk] (stride 0 to broadcast)");
   if (t->stride[3] != 1) return fail(SDPA_ERR_UNSUPPORTED, "bias key stride must be 1");
@@ -173,8 +178,8 @@ int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t S
   return SDPA_OK;
 }
 
-int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk, bool forward,
-              Ext* out) {
+int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int dtype,
+              bool forward, Ext* out) {
   Ext e;
   e.heads_total = H;
   if (ext != nullptr) {
@@ -196,7 +201,7 @@ int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
     if (e.rng_state != nullptr && e.rng_state == e.rng_used)
       return fail(SDPA_ERR_INVALID, "rng_state and rng_used must be distinct buffers");
     if (ext->bias != nullptr) {
-      const int rc = check_bias(ext->bias, B, H, Sq, Sk, &e);
+      const int rc = check_bias(ext->bias, B, H, Sq, Sk, dtype, &e);
       if (rc) return rc;
     }
   }
@@ -263,6 +268,7 @@ extern "C" {
 int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
              double dropout_p, int is_causal, double scale, const sdpa_tensor* out, float* lse,
              uint64_t* seed, uint64_t* offset, sdpa_stream_t stream) {
+  if (lse == nullptr) return fail(SDPA_ERR_INVALID, "lse is NULL");
   return sdpa_fwd_ext(q, k, v, dropout_p, is_causal, scale, out, lse, seed, offset, nullptr,
                       stream);
 }
@@ -279,14 +285,16 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   if ((rc = check_tensor(out, "out", &dout))) return rc;
   if ((rc = check_qkv(dq, dk, dv))) return rc;
   if (!same_shape(dq, dout)) return fail(SDPA_ERR_INVALID, "out must have q's shape");
-  if (lse == nullptr) return fail(SDPA_ERR_INVALID, "lse is NULL");
+  // lse may be NULL here: an inference-only forward writes no log-sum-exp.
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(SDPA_ERR_UNSUPPORTED, "lse is not 4-byte aligned");
   if ((rc = check_dropout(dropout_p))) return rc;
   float sc;
   if ((rc = resolve_scale(scale, dq.E, &sc))) return rc;
   Ext e;
-  if ((rc = check_ext(ext, dq.B, dq.H, dq.S, dk.S, true, &e))) return rc;
+  if (dk.dtype != dq.dtype || dv.dtype != dq.dtype || dout.dtype != dq.dtype)
+    return fail(SDPA_ERR_INVALID, "q, k, v and out must share one dtype");
+  if ((rc = check_ext(ext, dq.B, dq.H, dq.S, dk.S, dq.dtype, true, &e))) return rc;
   const bool drop = dropout_p > 0.0;
   const uint64_t advance = offset_advance(dq.B, e.heads_total, dq.S, dk.S);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -325,7 +333,8 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   p.bias = e.bias;
   p.sbias = e.sbias;
   const hipError_t err = timed_launch(SDPA_KERNEL_FWD, st, [&] {
-    return launch_fwd(p, (int)dq.E, is_causal != 0, drop, tile_choice(), st);
+    return launch_fwd(p, (int)dq.E, is_causal != 0, drop, dq.dtype == SDPA_F16, tile_choice(),
+                      st);
   });
   return hip_status(err, "forward launch");
 }
@@ -375,7 +384,10 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   if (workspace_bytes < bwd_workspace_bytes(dqi.B, dqi.H, dqi.S))
     return fail(SDPA_ERR_WORKSPACE, "workspace is smaller than sdpa_bwd_workspace_size()");
   Ext e;
-  if ((rc = check_ext(ext, dqi.B, dqi.H, dqi.S, dki.S, false, &e))) return rc;
+  for (const Desc* d : {&ddo, &dki, &dvi, &dout_i, &dqo, &dko, &dvo})
+    if (d->dtype != dqi.dtype)
+      return fail(SDPA_ERR_INVALID, "dout, q, k, v, out, dq, dk and dv must share one dtype");
+  if ((rc = check_ext(ext, dqi.B, dqi.H, dqi.S, dki.S, dqi.dtype, false, &e))) return rc;
 
   BwdParams p;
   p.q = dqi.ptr;
@@ -410,7 +422,10 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
-                                      [&] { return launch_bwd(p, E, causal, drop, st); });
+                                      [&] {
+                                        return launch_bwd(p, E, causal, drop,
+                                                          dqi.dtype == SDPA_F16, st);
+                                      });
   return hip_status(err, "backward launch");
 }
 

@@ -208,3 +208,15 @@ def test_zero_bias_equals_no_bias():
     assert (l1 - l2).abs().max().item() <= 1e-5
     for a, b in zip(g1, g2):
         assert (a.float() - b.float()).abs().max().item() <= 2e-2
+
+
+def test_inference_forward_without_lse():
+    say("inference forward: lse not written, out identical to the training forward")
+    q, k, v, _ = workloads.draw(2, 3, 300, 300, 64, 21, 1.0, "BHSE", device="cuda")
+    sdpa.sdpa_set_rng_state(3, 30)
+    o1, l1, s1, f1 = sdpa.sdpa_fwd_ext(q, k, v, 0.1, True, need_lse=False)
+    sdpa.sdpa_set_rng_state(3, 30)
+    o2, l2, s2, f2 = sdpa.sdpa_fwd(q, k, v, 0.1, True)
+    torch.cuda.synchronize()
+    assert l1 is None and (s1, f1) == (s2, f2)
+    assert torch.equal(o1, o2)

@@ -82,7 +82,9 @@ def _err(lib):
     (dict(scale=math.inf), bnd.SDPA_ERR_INVALID, "scale"),
     (dict(lse=0), bnd.SDPA_ERR_INVALID, "lse"),
     (dict(q=_t(S=0)), bnd.SDPA_ERR_INVALID, "size"),
-    (dict(q=_t(dtype=1)), bnd.SDPA_ERR_UNSUPPORTED, "dtype"),
+    (dict(q=_t(dtype=2)), bnd.SDPA_ERR_UNSUPPORTED, "dtype"),
+    (dict(q=_t(dtype=1)), bnd.SDPA_ERR_INVALID, "one dtype"),
+    (dict(q=_t(dtype=1), k=_t(dtype=1), v=_t(dtype=1)), bnd.SDPA_ERR_INVALID, "one dtype"),
     (dict(q=_t(E=32), k=_t(E=32), v=_t(E=32), out=_t(E=32)), bnd.SDPA_ERR_UNSUPPORTED, "head dim"),
     (dict(q=_t(stride=(2 * 128 * 64, 128 * 64, 1, 128))), bnd.SDPA_ERR_UNSUPPORTED, "stride"),
     (dict(q=_t(stride=(2 * 128 * 68, 128 * 68, 68, 1))), bnd.SDPA_ERR_UNSUPPORTED, "multiple of 8"),
@@ -115,6 +117,7 @@ def _bwd(lib, **over):
     (dict(lse=0), bnd.SDPA_ERR_INVALID),
     (dict(p=1.5), bnd.SDPA_ERR_INVALID),
     (dict(dv=_t(dtype=3)), bnd.SDPA_ERR_UNSUPPORTED),
+    (dict(dq=_t(dtype=1)), bnd.SDPA_ERR_INVALID),
     (dict(scale=-1.0), bnd.SDPA_ERR_INVALID),
     (dict(out=_t(stride=(2 * 128 * 64, 128 * 64, 64, 2))), bnd.SDPA_ERR_UNSUPPORTED),
 ])
