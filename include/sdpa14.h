@@ -152,7 +152,9 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       scale * q_i . k_j + bias[b, h, i, j] before masking and softmax, so the
  *       LSE includes it.  Logical shape [B, H, Sq, Sk], bf16, key stride 1,
  *       other strides >= 0 and multiples of 4 elements (0 broadcasts that
- *       dimension), data 8-byte aligned.  -inf entries hide a key; every row
+ *       dimension), data 8-byte aligned.  Reads go by aligned 8-byte granules,
+ *       so the rest of the granule holding a slice's last element is read
+ *       (and ignored).  -inf entries hide a key; every row
  *       must keep at least one visible key with a finite score.  Forward and
  *       backward must be given the same bias; its gradient is not computed.
  */

@@ -43,6 +43,16 @@
 namespace sdpa14 {
 namespace {
 
+// Bytes of one (batch, head) slice of the bias, rounded up to whole 8-byte
+// granules: a partially valid dword would otherwise read as zero under the
+// buffer range check.  The rounding stays inside the granule holding the last
+// element, so it never reaches another page.
+template <typename P>
+__device__ __forceinline__ uint32_t bias_bytes(const P& p) {
+  const int64_t b = ((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2;
+  return (uint32_t)((b + 7) & ~int64_t(7));
+}
+
 constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int E>
@@ -203,7 +213,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
   if (BIAS)
     br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
-                   (uint32_t)(((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2));
+                   bias_bytes(p));
   uint32_t bias_cur[16], bias_nxt[16];
   auto load_bias = [&](int t, uint32_t(&dst)[16]) {
     const int64_t row0 = (int64_t)(t0 + 2 * t + qs) * 32 + 4 * g;
@@ -450,7 +460,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
   if (BIAS)
     br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
-                   (uint32_t)(((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2));
+                   bias_bytes(p));
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   u32x2 bias_cur[4], bias_nxt[4];
   auto load_bias = [&](int t, u32x2(&dst)[4]) {

@@ -46,6 +46,16 @@
 namespace sdpa14 {
 namespace {
 
+// Bytes of one (batch, head) slice of the bias, rounded up to whole 8-byte
+// granules: a partially valid dword would otherwise read as zero under the
+// buffer range check.  The rounding stays inside the granule holding the last
+// element, so it never reaches another page.
+template <typename P>
+__device__ __forceinline__ uint32_t bias_bytes(const P& p) {
+  const int64_t b = ((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2;
+  return (uint32_t)((b + 7) & ~int64_t(7));
+}
+
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kRescaleSlack = 8.f;  // log2 units the reference max may lag
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   uint32_t brow = 0;
   if (BIAS) {
     br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
-                   (uint32_t)(((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2));
+                   bias_bytes(p));
     brow = (uint32_t)((int64_t)qrow * p.sbias.s * 2);
   }
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));

@@ -220,3 +220,62 @@ def test_inference_forward_without_lse():
     torch.cuda.synchronize()
     assert l1 is None and (s1, f1) == (s2, f2)
     assert torch.equal(o1, o2)
+
+
+def test_minus_infinity_bias_hides_keys_like_the_causal_mask():
+    say("bias of -inf above the diagonal equals causal masking")
+    B, H, S, E = 1, 2, 160, 64
+    q, k, v, do = workloads.draw(B, H, S, S, E, 24, 1.0, "BHSE", device="cuda")
+    tri = torch.ones(S, S, dtype=torch.bool, device="cuda").tril()
+    bias = torch.zeros(S, S, dtype=torch.bfloat16, device="cuda").masked_fill(~tri, float("-inf"))
+    o1, l1, s, f = sdpa.sdpa_fwd_ext(q, k, v, 0.0, False, bias=bias)
+    g1 = sdpa.sdpa_bwd_ext(do, q, k, v, o1, l1, 0.0, False, s, f, bias=bias)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = sdpa_ref.fwd(q, k, v, 0.0, True)
+    ref_g = sdpa_ref.bwd(do, q, k, v, 0.0, True)
+    assert_out(host64(o1), ref_out)
+    assert_lse(l1.cpu().double().numpy(), ref_lse)
+    assert_grads([(n, host64(a), r) for n, a, r in zip(("dq", "dk", "dv"), g1, ref_g)])
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (1, 37), (37, 1), (3, 200)])
+def test_bias_degenerate_sizes(Sq, Sk):
+    say(f"bias with Sq={Sq} Sk={Sk}")
+    B, H, E = 2, 2, 64
+    q, k, v, do = workloads.draw(B, H, Sq, Sk, E, 25, 1.0, "BHSE", device="cuda")
+    pad = (Sk + 3) // 4 * 4
+    g = torch.Generator("cpu").manual_seed(26)
+    bias = (torch.randn((B, 1, Sq, pad), generator=g)).to(torch.bfloat16).to("cuda")[..., :Sk]
+    for causal in (False, True):
+        out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, 0.0, causal, bias=bias)
+        grads = sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, 0.0, causal, s, o, bias=bias)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = sdpa_ref.fwd(q, k, v, 0.0, causal, bias=bias)
+        ref_g = sdpa_ref.bwd(do, q, k, v, 0.0, causal, bias=bias)
+        assert_out(host64(out), ref_out)
+        assert_lse(lse.cpu().double().numpy(), ref_lse)
+        assert_grads([(n, host64(a), r) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
+
+
+def test_everything_together_fp16_sharded_device_rng_bias():
+    say("fp16 + head shard + device RNG + bias + dropout against the whole-problem oracle")
+    B, H, S, E, p = 2, 4, 144, 64, 0.15
+    q, k, v, do = (t.to(torch.float16) for t in
+                   workloads.draw(B, H, S, S, E, 27, 1.0, "BHSE", device="cuda"))
+    g = torch.Generator("cpu").manual_seed(28)
+    bias = (torch.randn((1, H, S, S), generator=g)).to(torch.float16).to("cuda")
+    seed, off = 555, 64
+    ref_out, ref_lse = sdpa_ref.fwd(q, k, v, p, True, None, seed, off, bias=bias)
+    ref_g = sdpa_ref.bwd(do, q, k, v, p, True, seed, off, None, bias=bias)
+    h0, h1 = 1, 3
+    sl = (slice(None), slice(h0, h1))
+    state, used = _dev_state(seed, off), torch.zeros(2, dtype=torch.int64, device="cuda")
+    out, lse, _, _ = sdpa.sdpa_fwd_ext(q[sl], k[sl], v[sl], p, True, head_offset=h0, heads_total=H,
+                                       rng_state=state, rng_used=used, bias=bias[:, h0:h1])
+    grads = sdpa.sdpa_bwd_ext(do[sl], q[sl], k[sl], v[sl], out, lse, p, True, head_offset=h0,
+                              heads_total=H, rng_used=used, bias=bias[:, h0:h1])
+    torch.cuda.synchronize()
+    assert state.tolist() == [seed, off + philox_ref.offset_advance(B, H, S, S)]
+    assert_out(host64(out), ref_out[sl])
+    assert_lse(lse.cpu().double().numpy(), ref_lse[sl])
+    assert_grads([(n, host64(a), r[sl]) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
