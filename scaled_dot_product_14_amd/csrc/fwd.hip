@@ -90,8 +90,13 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   constexpr int NLD = KT_B / (NT * 16);  // loads per thread per tensor per stage
   constexpr int NPS = 2 * NLD;           // loads per thread per stage
   constexpr int CMB_FLOATS = (NS - 1) * NQ * (NEB * 16 + 2) * 64;  // merge buffer
-  constexpr int LDS_BYTES =
-      NSTAGE * STAGE > CMB_FLOATS * 4 ? NSTAGE * STAGE : CMB_FLOATS * 4;
+  // Per-wave bias scratch after the ring: 32 rows x 32 keys, rows padded to
+  // 72 bytes (8-byte aligned, at most two lanes of a 32-lane read per bank).
+  constexpr int BS_ROW_B = 72;
+  constexpr int BS_WAVE_B = 32 * BS_ROW_B;
+  constexpr int BS_OFF = NSTAGE * STAGE;
+  constexpr int RING_AND_BIAS = BS_OFF + (BIAS ? NW * BS_WAVE_B : 0);
+  constexpr int LDS_BYTES = RING_AND_BIAS > CMB_FLOATS * 4 ? RING_AND_BIAS : CMB_FLOATS * 4;
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
@@ -130,28 +135,29 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
     qf[es] = __builtin_bit_cast(
         bf16x8, buffer_load16(qr, (uint32_t)(((int64_t)qrow * p.sq.s + es * 16 + 8 * g) * 2)));
 
-  // Additive bias: the lane's query row, keys contiguous.  Register group cg of
-  // key block kb takes the four keys k0 + 32*kb + 8*cg + 4*g + 0..3 in one
-  // 8-byte load; the loads of tile it+1 go out at the start of step it.  Rows
-  // past Sq read zeros (those rows are never stored); keys past Sk are masked.
+  // Additive bias.  The wave's 32 rows x BN keys of tile t are fetched one step
+  // ahead with row-contiguous loads (lane l: row 16*i + l/4 of the wave's rows,
+  // keys 8*(l%4) .. +7 of a 32-key block, 16 bytes), then passed through a
+  // per-wave LDS scratch so that each lane reads its own row: register group cg
+  // of key block kb holds keys 32*kb + 8*cg + 4*g + 0..3.  Rows past Sq read
+  // zeros (never stored); keys past Sk are masked.
   __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
-  uint32_t brow = 0;
-  if (BIAS) {
-    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
-                   bias_bytes(p));
-    brow = (uint32_t)((int64_t)qrow * p.sbias.s * 2);
-  }
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 bias_cur[BN / 32][4], bias_nxt[BN / 32][4];
-  auto load_bias = [&](int t, u32x2(&dst)[BN / 32][4]) {
-    const uint32_t k0b = (uint32_t)((t * NS + ksp) * BN + 4 * g) * 2;
+  if (BIAS) br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h, bias_bytes(p));
+  const int bl_row = lane >> 2, bl_chunk = lane & 3;  // load pattern
+  uint4 bias_pf[BN / 32][2];
+  auto load_bias = [&](int t) {
+    const int64_t k0t = (int64_t)(t * NS + ksp) * BN + 8 * bl_chunk;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
-        dst[kb][cg] = __builtin_amdgcn_raw_buffer_load_b64(br, brow + k0b + (32 * kb + 8 * cg) * 2, 0, 0);
+      for (int i = 0; i < 2; ++i)
+        bias_pf[kb][i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       br, (uint32_t)(((int64_t)(q0 + 16 * i + bl_row) * p.sbias.s + k0t + 32 * kb) * 2),
+                       0, 0));
   };
-  if (BIAS && n_it > 0) load_bias(0, bias_cur);
+  unsigned char* bscr = lds + BS_OFF + wave * BS_WAVE_B;
+  if (BIAS && n_it > 0) load_bias(0);
 
   // K and V rows past kend read as zeros.  Stage it % NSTAGE of the ring holds
   // key rows it*ROWS .. it*ROWS + ROWS-1, loaded straight into LDS.
@@ -222,7 +228,24 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
     // Skip tiles past the key range and, when causal, above the diagonal.
     const bool active = (j < n_kt) && (!CAUSAL || k0 <= q0 + 31);
     const bool more = it + NSTAGE - 1 < n_it;
-    if (BIAS && it + 1 < n_it) load_bias(it + 1, bias_nxt);
+    // This step's prefetched bias, before the next tile's loads overwrite it.
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 bias_w[BN / 32][4];
+    if (BIAS && active) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          unsigned char* dst = bscr + (16 * i + bl_row) * BS_ROW_B + 16 * bl_chunk;
+          *reinterpret_cast<uint2*>(dst) = make_uint2(bias_pf[kb][i].x, bias_pf[kb][i].y);
+          *reinterpret_cast<uint2*>(dst + 8) = make_uint2(bias_pf[kb][i].z, bias_pf[kb][i].w);
+        }
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg)
+          bias_w[kb][cg] = lds_at<u32x2>(bscr, l32 * BS_ROW_B + 16 * cg + 8 * g);
+      }
+    }
+    if (BIAS && it + 1 < n_it) load_bias(it + 1);
     if (!active && more) issue(it + NSTAGE - 1);
     if (active) {
       const unsigned char* st = stage(it);
@@ -236,7 +259,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
         if (BIAS) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const uint32_t w = bias_cur[kb][r >> 2][(r >> 1) & 1];
+            const uint32_t w = bias_w[kb][r >> 2][(r >> 1) & 1];
             s[kb][r] = from16<F16>((r & 1) ? (w >> 16) : w) * inv_scale;
           }
         }
@@ -313,12 +336,6 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
           const int o0 = troff[0][eb] + 16 * ksx * ROW_B, o1 = troff[1][eb] + 16 * ksx * ROW_B;
           oacc[eb] = mfma16<F16>(tr_pair(st, o0, o1), pb[ksx], oacc[eb]);
         }
-    }
-    if (BIAS) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) bias_cur[kb][cg] = bias_nxt[kb][cg];
     }
     // The next stage must have landed; this one is free once every wave is past here.
     if (NSTAGE == 3 && it + 2 < n_it)
