@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache kernel timing (input sets rotated past the caches)")
     ap.add_argument("--bias", choices=("none", "qk", "bhqk"), default="none",
                     help="add an additive bf16 bias: [Sq, Sk] broadcast over batch and heads, "
                          "or a full [B, H, Sq, Sk] (drawn N(0, 4)); timed through the extended calls")
@@ -268,6 +270,37 @@ def main():
         kern[name] = {"avg_us": tot / max(n, 1) * 1e3, "launches": n}
     log(f"kernel averages (us): { {k_: round(v_['avg_us'], 2) for k_, v_ in kern.items()} }")
 
+    # Cold cache: the same kernels on input sets rotated so that each launch
+    # finds its inputs outside the 4 MB L2s and the 256 MB last-level cache
+    # (more than 512 MB of distinct inputs per rotation).
+    cold = None
+    if not args.no_cold and bias is None:
+        set_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, do, out))
+        n_sets = max(2, -(-2 * 256 * 2**20 // set_bytes) + 1)
+        sets = []
+        for i in range(n_sets):
+            qi, ki, vi, doi = (t.clone() for t in (q, k, v, do))
+            sets.append((qi, ki, vi, doi, torch.empty_like(q),
+                         torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device="cuda")))
+        for kind in names:
+            sdpa.sdpa_profile_read(kind)
+        sdpa.sdpa_profile_enable(True)
+        reps = max(1, 200 // n_sets)
+        for _ in range(reps):
+            for qi, ki, vi, doi, oi, li in sets:
+                _, _, s_, o_ = sdpa.sdpa_fwd(qi, ki, vi, w.dropout_p, w.causal, None, out=oi, lse=li)
+                sdpa.sdpa_bwd(doi, qi, ki, vi, oi, li, w.dropout_p, w.causal, s_, o_, None, dq=dq,
+                              dk=dk, dv=dv, workspace=ws)
+        torch.cuda.synchronize()
+        sdpa.sdpa_profile_enable(False)
+        cold = {"input_sets": n_sets, "bytes_per_set": set_bytes}
+        for kind, name in names.items():
+            tot, n = sdpa.sdpa_profile_read(kind)
+            cold[name + "_avg_us"] = tot / max(n, 1) * 1e3
+        del sets
+        log(f"cold-cache kernel averages (us): fwd {cold['fwd_avg_us']:.2f}, "
+            f"bwd {cold['bwd_avg_us']:.2f} over {n_sets} input sets")
+
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
     kern["fwd"]["algorithmic_tflop"] = f_fwd / 1e12
     kern["bwd"]["algorithmic_tflop"] = f_bwd / 1e12
@@ -305,6 +338,7 @@ def main():
         "bwd": {"tflops": f_bwd / (ms_bwd * 1e-3) / 1e12, "us": ms_bwd * 1e3,
                 "frac_peak": f_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernels": kern,
+        "kernels_cold_cache": cold,
         "roofline": roof,
         "cpu_baseline": None,
     }
