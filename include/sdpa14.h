@@ -151,8 +151,8 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       mem eff" announces for the memory-efficient kernel: the scores become
  *       scale * q_i . k_j + bias[b, h, i, j] before masking and softmax, so the
  *       LSE includes it.  Logical shape [B, H, Sq, Sk], bf16, key stride 1,
- *       other strides >= 0 and multiples of 4 elements (0 broadcasts that
- *       dimension), data 8-byte aligned.  Reads go by aligned 8-byte granules,
+ *       other strides >= 0 and multiples of 8 elements (0 broadcasts that
+ *       dimension), data 16-byte aligned.  Reads go by aligned 8-byte granules,
  *       so the rest of the granule holding a slice's last element is read
  *       (and ignored).  -inf entries hide a key; every row
  *       must keep at least one visible key with a finite score.  Forward and

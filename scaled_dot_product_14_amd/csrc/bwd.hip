@@ -55,7 +55,7 @@ __device__ __forceinline__ uint32_t bias_bytes(const P& p) {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int E>
+template <int E, bool BIAS>
 struct BwdCfg {
   static constexpr int NES = E / 16;  // 16-wide contraction steps over E
   static constexpr int NEB = E / 32;  // 32-wide output blocks over E
@@ -65,11 +65,15 @@ struct BwdCfg {
   static constexpr int NLD = TILE_B / (256 * 16);  // LDS-DMA loads per thread per tile
   static_assert(NLD == E / 64, "tile loads");
   static constexpr int DL_B = 64 * 8;              // -D and L of the pair's 64 rows
-  static constexpr int STAGE_A = 4 * TILE_B + DL_B;  // Q, Q', dO, dO', -D, L
-  static constexpr int STAGE_B = 4 * TILE_B;         // K, K', V, V'
+  // With a bias, each stage also holds the 64 x 64 block of it that the step
+  // needs (rows of 128 bytes, laid out like a head-dim-64 tile), 2 loads per thread.
+  static constexpr int BIAS_B = BIAS ? 64 * 128 : 0;
+  static constexpr int NBL = BIAS ? 2 : 0;
+  static constexpr int STAGE_A = 4 * TILE_B + DL_B + BIAS_B;  // Q, Q', dO, dO', -D, L, bias
+  static constexpr int STAGE_B = 4 * TILE_B + BIAS_B;         // K, K', V, V', bias
   static constexpr int NSTAGE = 3;
-  static constexpr int NPAIR_A = 4 * NLD + 1;  // loads per thread per stage, dK/dV role
-  static constexpr int NPAIR_B = 4 * NLD;      // loads per thread per stage, dQ role
+  static constexpr int NPAIR_A = 4 * NLD + 1 + NBL;  // loads per thread per stage, dK/dV role
+  static constexpr int NPAIR_B = 4 * NLD + NBL;      // loads per thread per stage, dQ role
   static constexpr int RED_B = 4 * NEB * 16 * 64 * 4;  // end-of-block exchange
   static constexpr int LDS_B = NSTAGE * STAGE_A;
   // The dQ role's stage 2 also takes the block's (D, L) in the prologue.
@@ -171,9 +175,9 @@ __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], flo
 template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                                           unsigned char* lds) {
-  using C = BwdCfg<E>;
+  using C = BwdCfg<E, BIAS>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
-  constexpr int ST_Q = 0, ST_DO = 2 * TILE_B, ST_DL = 4 * TILE_B;
+  constexpr int ST_Q = 0, ST_DO = 2 * TILE_B, ST_DL = 4 * TILE_B, ST_BIAS = ST_DL + C::DL_B;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int sb = wave & 1, qs = wave >> 1;
@@ -206,23 +210,16 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const int t0 = CAUSAL ? min(kb0 / 32, nqt) : 0;
   const int n_it = (nqt - t0 + 1) / 2;
 
-  // Additive bias at (row q0 + 8*cg + 4*g + u, this lane's key) for register
-  // 4*cg + u, one 2-byte load each (the 32 lanes of a half read 64 contiguous
-  // bytes of one row); step it+1's values are loaded at the start of step it.
-  // Rows past Sq read zeros, keys past Sk are masked.
+  // Additive bias: stage it also holds the bias block of its 64 query rows x
+  // this workgroup's 64 keys; a lane reads its key's values for rows
+  // 8*cg + 4*g + 0..3 with one transposed read per register group.
   __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
-  if (BIAS)
-    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
-                   bias_bytes(p));
-  uint32_t bias_cur[16], bias_nxt[16];
-  auto load_bias = [&](int t, uint32_t(&dst)[16]) {
-    const int64_t row0 = (int64_t)(t0 + 2 * t + qs) * 32 + 4 * g;
+  uint32_t obias[2] = {0u, 0u};
+  if (BIAS) {
+    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h, bias_bytes(p));
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      dst[r] = __builtin_amdgcn_raw_buffer_load_b16(
-          br, (uint32_t)(((row0 + 8 * (r >> 2) + (r & 3)) * p.sbias.s + key) * 2), 0, 0);
-  };
-  if (BIAS && n_it > 0) load_bias(0, bias_cur);
+    for (int k = 0; k < 2; ++k) obias[k] = dma_src_offset<64>(k, tid, p.sbias.s) + (uint32_t)kb0 * 2u;
+  }
 
   // Stage it % 3 of the ring holds query tiles t0 + 2*it and t0 + 2*it + 1.
   uint32_t oq[NLD], odo[NLD];
@@ -232,7 +229,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     odo[k] = dma_src_offset<E>(k, tid, p.sdo.s);
   }
   // Load idx (0 .. NPAIR_A-1) of stage it: (half, tensor, k) for the Q and dO
-  // tiles, then -D (waves 0, 1) and L (waves 2, 3) of the pair's 64 rows.
+  // tiles, then -D (waves 0, 1) and L (waves 2, 3) of the pair's 64 rows, then
+  // the two loads of the bias block.
   auto issue_one = [&](int it, int idx, float after) {
     unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
     const uint32_t row0 = (uint32_t)((t0 + 2 * it) * 32);
@@ -244,9 +242,14 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
         dma16_after(rdo, dst, r * (uint32_t)(p.sdo.s * 2) + odo[k], after);
       else
         dma16_after(rq, dst, r * (uint32_t)(p.sq.s * 2) + oq[k], after);
-    } else if (lane < 8) {
-      dma16_after(rdl, st + ST_DL + wave * 128,
-                  row0 * 4u + (uint32_t)((wave & 1) * 128 + lane * 16), after);
+    } else if (idx == 4 * NLD) {
+      if (lane < 8)
+        dma16_after(rdl, st + ST_DL + wave * 128,
+                    row0 * 4u + (uint32_t)((wave & 1) * 128 + lane * 16), after);
+    } else {
+      const int k = idx - 4 * NLD - 1;
+      dma16_after(br, st + ST_BIAS + k * 4096 + wave * 1024,
+                  row0 * (uint32_t)(p.sbias.s * 2) + obias[k], after);
     }
   };
   // The loads of a stage are spread over the step in NSLOT groups, each placed
@@ -316,7 +319,6 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     const int q0 = (t0 + 2 * it + qs) * 32;
     // Skip tiles past Sq and, when causal, tiles whose rows all precede the keys.
     const bool active = !(q0 >= p.Sq || (CAUSAL && q0 + 31 < kbs));
-    if (BIAS && it + 1 < n_it) load_bias(it + 1, bias_nxt);
     // Every step issues the loads of stage it+2, also past the last stage (those
     // rows lie past Sq and read as zeros into a stage nobody reads again), so
     // the issue points need no branch and every barrier waits the same count.
@@ -338,8 +340,15 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
       // A bias enters as L - log2(e) * bias, per element.
       if (BIAS) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          l4[r >> 2][r & 3] = fmaf(from16<F16>(bias_cur[r]), -kLog2e, l4[r >> 2][r & 3]);
+        for (int cg = 0; cg < 4; ++cg) {
+          const bf16x4 bv = lds_tr4(reinterpret_cast<const uint16_t*>(
+              st + ST_BIAS + tr_off<64>(qs * 32 + 8 * cg + tr_row, sb * 32 + tr_col)));
+          const uint2 w = __builtin_bit_cast(uint2, bv);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            l4[cg][u] = fmaf(from16<F16>((u & 1) ? ((u < 2 ? w.x : w.y) >> 16) : (u < 2 ? w.x : w.y)),
+                             -kLog2e, l4[cg][u]);
+        }
       }
       f32x16 sacc = zero16(), dpacc;
 #pragma unroll
@@ -398,10 +407,6 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
           if (hf == 1 && (eb == 0 || eb == NEB - 1)) issue_slot(it + 2, eb == 0 ? 3 : 4, 0.f);
         }
     }
-    if (BIAS) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) bias_cur[r] = bias_nxt[r];
-    }
     // Stage it+1 must have landed; stage it is free once every wave is past here.
     ring_barrier<C::NPAIR_A>();
   }
@@ -424,9 +429,9 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
 // ---------------------------------------------------------------------------
 template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
-  using C = BwdCfg<E>;
+  using C = BwdCfg<E, BIAS>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
-  constexpr int ST_K = 0, ST_V = 2 * TILE_B;
+  constexpr int ST_K = 0, ST_V = 2 * TILE_B, ST_BIAS = 4 * TILE_B;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int qsb = wave & 1, ks = wave >> 1;
@@ -454,22 +459,17 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int kt_end = CAUSAL ? min(nkt, min(q0b + 63, p.Sq - 1) / 32 + 1) : nkt;
   const int n_it = (kt_end + 1) / 2;
 
-  // Additive bias on the row's keys k0 + 8*cg + 4*g + 0..3 (register group cg),
-  // one 8-byte load per group; step it+1's values are loaded at the start of
-  // step it.  Rows past Sq read zeros, keys past Sk are masked.
+  // Additive bias: stage it also holds the bias block of this workgroup's 64
+  // rows x the stage's 64 keys; a lane reads keys 8*cg + 4*g + 0..3 of its
+  // row (8 bytes) for register group cg.
   __amdgpu_buffer_rsrc_t br = make_rsrc(p.q, 0u);
-  if (BIAS)
-    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h,
-                   bias_bytes(p));
-  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-  u32x2 bias_cur[4], bias_nxt[4];
-  auto load_bias = [&](int t, u32x2(&dst)[4]) {
-    const int64_t base = (int64_t)qrow * p.sbias.s + (2 * t + ks) * 32 + 4 * g;
+  uint32_t obias[2] = {0u, 0u};
+  if (BIAS) {
+    br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h, bias_bytes(p));
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg)
-      dst[cg] = __builtin_amdgcn_raw_buffer_load_b64(br, (uint32_t)((base + 8 * cg) * 2), 0, 0);
-  };
-  if (BIAS && n_it > 0) load_bias(0, bias_cur);
+    for (int k = 0; k < 2; ++k)
+      obias[k] = dma_src_offset<64>(k, tid, p.sbias.s) + (uint32_t)q0b * (uint32_t)(p.sbias.s * 2);
+  }
 
   // Stage it % 3 of the ring holds key tiles 2*it and 2*it + 1.
   uint32_t okk[NLD], ov[NLD];
@@ -478,9 +478,16 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     okk[k] = dma_src_offset<E>(k, tid, p.sk.s);
     ov[k] = dma_src_offset<E>(k, tid, p.sv.s);
   }
-  // Load idx (0 .. NPAIR_B-1) of stage it: (half, tensor, k) for the K and V tiles.
+  // Load idx (0 .. NPAIR_B-1) of stage it: (half, tensor, k) for the K and V
+  // tiles, then the two loads of the bias block.
   auto issue_one = [&](int it, int idx, float after) {
     unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
+    if (idx >= 4 * NLD) {
+      const int k = idx - 4 * NLD;
+      dma16_after(br, st + ST_BIAS + k * 4096 + wave * 1024, (uint32_t)(128 * it) + obias[k],
+                  after);
+      return;
+    }
     const int half = idx / (2 * NLD), tensor = (idx / NLD) & 1, k = idx % NLD;
     const uint32_t r = (uint32_t)(64 * it) + 32u * half;
     unsigned char* dst = st + (tensor ? ST_V : ST_K) + half * TILE_B + k * 4096 + wave * 1024;
@@ -566,7 +573,6 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     const int j = 2 * it + ks;
     const int k0 = j * 32;
     const bool active = !(j >= kt_end || (CAUSAL && k0 > q0 + 31));
-    if (BIAS && it + 1 < n_it) load_bias(it + 1, bias_nxt);
     // Loads of stage it+2 on every step, as in the dK/dV role (past the last
     // stage they fetch rows nobody reads).
     if (!active) issue(it + 2);
@@ -578,11 +584,18 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
       // L of the row, minus log2(e) * bias per element when there is a bias.
       float lb[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        lb[r] = lse2;
-        if (BIAS) {
-          const uint32_t w = bias_cur[r >> 2][(r >> 1) & 1];
-          lb[r] = fmaf(from16<F16>((r & 1) ? (w >> 16) : w), -kLog2e, lse2);
+      for (int r = 0; r < 16; ++r) lb[r] = lse2;
+      if (BIAS) {
+        const int brow = qsb * 32 + l32;
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) {
+          const uint2 w = lds_at<uint2>(
+              st, ST_BIAS + brow * 128 + (((4 * ks + cg) ^ tile_swz<64>(brow)) << 4) + 8 * g);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t x = u < 2 ? w.x : w.y;
+            lb[4 * cg + u] = fmaf(from16<F16>((u & 1) ? (x >> 16) : x), -kLog2e, lse2);
+          }
         }
       }
       // S^T, dP^T: lane = row, register r = key k0 + 8*(r/4) + 4*g + r%4.
@@ -638,10 +651,6 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
           if (hf == 1 && eb == 0) issue_slot(it + 2, 3, 0.f);
         }
     }
-    if (BIAS) {
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg) bias_cur[cg] = bias_nxt[cg];
-    }
     ring_barrier<C::NPAIR_B>();
   }
   ring_barrier<0>();  // the trailing loads have landed before the stages are reused
@@ -659,7 +668,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 // blocks first; all blocks of a head sit on one XCD when the head count allows.
 template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E>::LDS_B];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E, BIAS>::LDS_B];
   const int bh_count = p.B * p.H;
   int bh, slot;
   if ((bh_count & 7) == 0) {

@@ -167,10 +167,10 @@ int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t S
     return fail(SDPA_ERR_INVALID, "bias must have logical shape [B, H, Sq, Sk] (stride 0 to broadcast)");
   if (t->stride[3] != 1) return fail(SDPA_ERR_UNSUPPORTED, "bias key stride must be 1");
   for (int i = 0; i < 3; ++i)
-    if (t->stride[i] < 0 || t->stride[i] % 4 != 0)
-      return fail(SDPA_ERR_UNSUPPORTED, "bias strides must be >= 0 and multiples of 4 elements");
-  if (reinterpret_cast<uintptr_t>(t->data) % 8 != 0)
-    return fail(SDPA_ERR_UNSUPPORTED, "bias data is not 8-byte aligned");
+    if (t->stride[i] < 0 || t->stride[i] % 8 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "bias strides must be >= 0 and multiples of 8 elements");
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "bias data is not 16-byte aligned");
   if (((Sq + 128) * t->stride[2] + Sk) * 2 >= (int64_t(1) << 31))
     return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice of the bias spans 2 GiB or more");
   e->bias = static_cast<const uint16_t*>(t->data);

@@ -174,9 +174,9 @@ def _bias(size=(1, 2, 128, 128), stride=(0, 128 * 128, 128, 1), data=FAKE, dtype
     (_ext(bias=_bias(dtype=1)), bnd.SDPA_ERR_UNSUPPORTED, "bias dtype"),
     (_ext(bias=_bias(size=(1, 2, 128, 64))), bnd.SDPA_ERR_INVALID, "shape"),
     (_ext(bias=_bias(stride=(0, 0, 1, 128))), bnd.SDPA_ERR_UNSUPPORTED, "key stride"),
-    (_ext(bias=_bias(stride=(0, 0, 130, 1))), bnd.SDPA_ERR_UNSUPPORTED, "multiples of 4"),
+    (_ext(bias=_bias(stride=(0, 0, 132, 1))), bnd.SDPA_ERR_UNSUPPORTED, "multiples of 8"),
     (_ext(bias=_bias(stride=(0, -128, 128, 1))), bnd.SDPA_ERR_UNSUPPORTED, ">= 0"),
-    (_ext(bias=_bias(data=FAKE + 2)), bnd.SDPA_ERR_UNSUPPORTED, "8-byte"),
+    (_ext(bias=_bias(data=FAKE + 8)), bnd.SDPA_ERR_UNSUPPORTED, "16-byte"),
     (_ext(bias=_bias(stride=(0, 0, 1 << 24, 1))), bnd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
 ])
 def test_forward_ext_rejects_bad_options(lib, ext, code, needle):
