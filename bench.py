@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time spent on the oracle baseline")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--keep-bits", action="store_true",
+                    help="with dropout: the forward keeps its mask bits for the backward "
+                         "(extended calls) instead of the backward regenerating them")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache kernel timing (input sets rotated past the caches)")
     ap.add_argument("--bias", choices=("none", "qk", "bhqk"), default="none",
@@ -205,22 +208,27 @@ def main():
         bshape = (w.Sq, w.Sk) if args.bias == "qk" else (w.B, w.H, w.Sq, w.Sk)
         bias = (torch.randn(bshape, generator=gb) * 2.0).to(torch.bfloat16).to("cuda")
 
+    keep = None
+    if args.keep_bits:
+        keep = torch.empty(sdpa.sdpa_keep_bits_size(w.B, w.H, w.Sq, w.Sk) // 4, dtype=torch.int32,
+                           device="cuda")
+
     def fwd():
-        if bias is None:
+        if bias is None and keep is None:
             _, _, s, o = sdpa.sdpa_fwd(q, k, v, w.dropout_p, w.causal, None, out=out, lse=lse)
         else:
             _, _, s, o = sdpa.sdpa_fwd_ext(q, k, v, w.dropout_p, w.causal, None, out=out,
-                                           lse=lse, bias=bias)
+                                           lse=lse, bias=bias, keep_bits=keep)
         state["so"] = (s, o)
 
     def bwd():
         s, o = state["so"]
-        if bias is None:
+        if bias is None and keep is None:
             sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
                           dk=dk, dv=dv, workspace=ws)
         else:
             sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
-                              dk=dk, dv=dv, workspace=ws, bias=bias)
+                              dk=dk, dv=dv, workspace=ws, bias=bias, keep_bits=keep)
 
     def step():
         fwd()
@@ -274,7 +282,7 @@ def main():
     # finds its inputs outside the 4 MB L2s and the 256 MB last-level cache
     # (more than 512 MB of distinct inputs per rotation).
     cold = None
-    if not args.no_cold and bias is None:
+    if not args.no_cold and bias is None and keep is None:
         set_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, do, out))
         n_sets = max(2, -(-2 * 256 * 2**20 // set_bytes) + 1)
         sets = []
@@ -312,7 +320,7 @@ def main():
     dk_ = kern[dominant]
     roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
-            "traffic": measured_traffic(w.name, dominant) if bias is None else None}
+            "traffic": measured_traffic(w.name, dominant) if bias is None and keep is None else None}
 
     result = {
         "metric": METRIC,
@@ -329,7 +337,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "E": w.E,
                    "layout": w.layout, "causal": w.causal, "dropout_p": w.dropout_p,
-                   "bias": args.bias, "cache": "warm (same buffers every step)"},
+                   "bias": args.bias, "keep_bits": bool(args.keep_bits),
+                   "cache": "warm (same buffers every step)"},
         "timing": "graph replay of the captured step (eager_ms_per_step: the same step "
                   "issued from Python each time)",
         "eager_ms_per_step": ms_eager,

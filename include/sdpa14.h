@@ -157,6 +157,14 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       (and ignored).  -inf entries hide a key; every row
  *       must keep at least one visible key with a finite score.  Forward and
  *       backward must be given the same bias; its gradient is not computed.
+ *   keep_bits  (NULL for none; used only when dropout_p > 0)
+ *       Device buffer of sdpa_keep_bits_size(B, H, Sq, Sk) bytes, 16-byte
+ *       aligned.  The forward writes the dropout keep bits it draws there (bit
+ *       j % 32 of word j / 32 of row (b, h, i), rows of ceil(ceil(Sk/32)/4)*4
+ *       words; bits of keys a row cannot see are left unspecified), and a
+ *       backward given the same buffer reads them instead of regenerating the
+ *       Philox stream in each of its two workgroup roles.  The buffer must
+ *       come from the forward with the same inputs, seed and offset, unchanged.
  */
 typedef struct sdpa_ext {
   int64_t head_offset;
@@ -164,6 +172,7 @@ typedef struct sdpa_ext {
   uint64_t* rng_state;
   uint64_t* rng_used;
   const sdpa_tensor* bias;
+  uint32_t* keep_bits;
 } sdpa_ext;
 
 /* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL.
@@ -180,6 +189,10 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
                  const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
                  void* workspace, size_t workspace_bytes, const sdpa_ext* ext,
                  sdpa_stream_t stream);
+
+/* Bytes of the keep-bit cache (sdpa_ext.keep_bits) for a problem; 0 when a size
+ * is not positive. */
+size_t sdpa_keep_bits_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk);
 
 /* Workspace bytes sdpa_bwd needs for B*H*Sq query rows (8 per row, rounded up to
  * 256); 0 when a size is not positive. */

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     sdpa_fwd,
     sdpa_fwd_ext,
     sdpa_get_rng_state,
+    sdpa_keep_bits_size,
     sdpa_profile_enable,
     sdpa_profile_read,
     sdpa_set_rng_state,

@@ -29,6 +29,7 @@ KERNEL_BWD = 1
 
 EXPORTED = (
     "sdpa_fwd", "sdpa_bwd", "sdpa_fwd_ext", "sdpa_bwd_ext", "sdpa_bwd_workspace_size",
+    "sdpa_keep_bits_size",
     "sdpa_set_rng_state",
     "sdpa_get_rng_state", "sdpa_status_string", "sdpa_last_error",
     "sdpa_debug_dropout_mask", "sdpa_profile_enable", "sdpa_profile_read",
@@ -51,6 +52,7 @@ class SdpaExt(ctypes.Structure):
         ("rng_state", ctypes.c_void_p),
         ("rng_used", ctypes.c_void_p),
         ("bias", ctypes.POINTER(SdpaTensor)),
+        ("keep_bits", ctypes.c_void_p),
     ]
 
 
@@ -88,6 +90,8 @@ def load_library(path: str = LIB_PATH):
                                  ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, P, P, P,
                                  ctypes.c_void_p, ctypes.c_size_t, E, ctypes.c_void_p]
     lib.sdpa_bwd_ext.restype = ctypes.c_int
+    lib.sdpa_keep_bits_size.argtypes = [ctypes.c_int64] * 4
+    lib.sdpa_keep_bits_size.restype = ctypes.c_size_t
     lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.sdpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.sdpa_set_rng_state.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
@@ -211,9 +215,19 @@ def _rng_buffer(t, name: str):
     return t.data_ptr()
 
 
-def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None):
+def sdpa_keep_bits_size(B: int, H: int, Sq: int, Sk: int) -> int:
+    """Bytes of the dropout keep-bit cache ``sdpa_fwd_ext``/``sdpa_bwd_ext`` can share."""
+    return int(load_library().sdpa_keep_bits_size(int(B), int(H), int(Sq), int(Sk)))
+
+
+def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None, keep_bits=None):
     """The options block and the objects it points into (keep both alive for the call)."""
     e = SdpaExt()
+    if keep_bits is not None:
+        if not (isinstance(keep_bits, torch.Tensor) and keep_bits.is_cuda
+                and keep_bits.is_contiguous()):
+            raise ValueError("keep_bits must be a contiguous device tensor")
+        e.keep_bits = keep_bits.data_ptr()
     e.head_offset = int(head_offset)
     e.heads_total = int(heads_total)
     e.rng_state = _rng_buffer(rng_state, "rng_state")
@@ -231,7 +245,8 @@ def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None):
 
 def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale=None,
                  out=None, lse=None, *, head_offset: int = 0, heads_total: int = 0,
-                 rng_state=None, rng_used=None, bias=None, need_lse: bool = True):
+                 rng_state=None, rng_used=None, bias=None, need_lse: bool = True,
+                 keep_bits=None):
     """Forward with options: returns ``(out, lse, seed, offset)``.
 
     ``head_offset`` / ``heads_total`` place the call's heads in a larger problem
@@ -241,7 +256,8 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
     used land in ``rng_used``.  ``bias`` (bf16, broadcastable to
     [B, H, Sq, Sk], key dimension contiguous) is added to the scaled scores.
     ``need_lse=False`` runs the inference-only forward: no log-sum-exp is
-    written and ``lse`` is returned as None.
+    written and ``lse`` is returned as None.  ``keep_bits`` (a device buffer of
+    ``sdpa_keep_bits_size`` bytes) receives the dropout keep bits for a backward.
     """
     lib = load_library()
     if out is None:
@@ -255,7 +271,7 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
         lse = None
     dq_, dk_, dv_, do_ = describe(q), describe(k), describe(v), describe(out)
     ext, _keep = _ext(head_offset, heads_total, rng_state, rng_used, bias,
-                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]))
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits)
     seed, offset = ctypes.c_uint64(), ctypes.c_uint64()
     with torch.cuda.device(q.device):
         rc = lib.sdpa_fwd_ext(ctypes.byref(dq_), ctypes.byref(dk_), ctypes.byref(dv_),
@@ -271,7 +287,8 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
 
 def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int = 0,
                  offset: int = 0, scale=None, dq=None, dk=None, dv=None, workspace=None, *,
-                 head_offset: int = 0, heads_total: int = 0, rng_used=None, bias=None):
+                 head_offset: int = 0, heads_total: int = 0, rng_used=None, bias=None,
+                 keep_bits=None):
     """Backward with options (see ``sdpa_fwd_ext``): returns ``(dq, dk, dv)``.
 
     With ``rng_used`` the kernels read (seed, offset) from that device tensor
@@ -287,7 +304,7 @@ def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, see
                                 dtype=torch.uint8, device=q.device)
     descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
     ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
-                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]))
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits)
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd_ext(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                               float(dropout_p), int(bool(is_causal)), int(seed), int(offset),

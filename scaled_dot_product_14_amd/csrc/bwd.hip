@@ -55,7 +55,7 @@ __device__ __forceinline__ uint32_t bias_bytes(const P& p) {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int E, bool BIAS>
+template <int E, bool BIAS, bool KEEP>
 struct BwdCfg {
   static constexpr int NES = E / 16;  // 16-wide contraction steps over E
   static constexpr int NEB = E / 32;  // 32-wide output blocks over E
@@ -69,11 +69,15 @@ struct BwdCfg {
   // needs (rows of 128 bytes, laid out like a head-dim-64 tile), 2 loads per thread.
   static constexpr int BIAS_B = BIAS ? 64 * 128 : 0;
   static constexpr int NBL = BIAS ? 2 : 0;
-  static constexpr int STAGE_A = 4 * TILE_B + DL_B + BIAS_B;  // Q, Q', dO, dO', -D, L, bias
-  static constexpr int STAGE_B = 4 * TILE_B + BIAS_B;         // K, K', V, V', bias
+  // With the forward's keep bits, each stage holds 16 bytes (four 32-key words)
+  // of each of its 64 rows, one load by 16 lanes of each wave.
+  static constexpr int KEEP_B = KEEP ? 64 * 16 : 0;
+  static constexpr int NKL = KEEP ? 1 : 0;
+  static constexpr int STAGE_A = 4 * TILE_B + DL_B + BIAS_B + KEEP_B;  // Q, Q', dO, dO', -D, L, bias, bits
+  static constexpr int STAGE_B = 4 * TILE_B + BIAS_B + KEEP_B;         // K, K', V, V', bias, bits
   static constexpr int NSTAGE = 3;
-  static constexpr int NPAIR_A = 4 * NLD + 1 + NBL;  // loads per thread per stage, dK/dV role
-  static constexpr int NPAIR_B = 4 * NLD + NBL;      // loads per thread per stage, dQ role
+  static constexpr int NPAIR_A = 4 * NLD + 1 + NBL + NKL;  // loads per thread per stage, dK/dV role
+  static constexpr int NPAIR_B = 4 * NLD + NBL + NKL;      // loads per thread per stage, dQ role
   static constexpr int RED_B = 4 * NEB * 16 * 64 * 4;  // end-of-block exchange
   static constexpr int LDS_B = NSTAGE * STAGE_A;
   // The dQ role's stage 2 also takes the block's (D, L) in the prologue.
@@ -172,12 +176,13 @@ __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], flo
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
 __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                                           unsigned char* lds) {
-  using C = BwdCfg<E, BIAS>;
+  using C = BwdCfg<E, BIAS, KEEP>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
   constexpr int ST_Q = 0, ST_DO = 2 * TILE_B, ST_DL = 4 * TILE_B, ST_BIAS = ST_DL + C::DL_B;
+  constexpr int ST_KEEP = ST_BIAS + C::BIAS_B;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int sb = wave & 1, qs = wave >> 1;
@@ -210,6 +215,14 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   const int t0 = CAUSAL ? min(kb0 / 32, nqt) : 0;
   const int n_it = (nqt - t0 + 1) / 2;
 
+  // Keep bits from the forward: stage it holds, for each of its 64 rows, the
+  // 16-byte chunk of words that contains this workgroup's two 32-key words.
+  __amdgpu_buffer_rsrc_t rkeep = make_rsrc(p.q, 0u);
+  uint32_t okeep = 0u;
+  if (KEEP) {
+    rkeep = make_rsrc(p.keep + (int64_t)bh * p.Sq * p.keep_w, (uint32_t)(p.Sq * p.keep_w * 4));
+    okeep = (uint32_t)((wave * 16 + (lane & 15)) * p.keep_w * 4 + (kblk >> 1) * 16);
+  }
   // Additive bias: stage it also holds the bias block of its 64 query rows x
   // this workgroup's 64 keys; a lane reads its key's values for rows
   // 8*cg + 4*g + 0..3 with one transposed read per register group.
@@ -246,10 +259,12 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
       if (lane < 8)
         dma16_after(rdl, st + ST_DL + wave * 128,
                     row0 * 4u + (uint32_t)((wave & 1) * 128 + lane * 16), after);
-    } else {
+    } else if (BIAS && idx < 4 * NLD + 1 + C::NBL) {
       const int k = idx - 4 * NLD - 1;
       dma16_after(br, st + ST_BIAS + k * 4096 + wave * 1024,
                   row0 * (uint32_t)(p.sbias.s * 2) + obias[k], after);
+    } else if (lane < 16) {
+      dma16_after(rkeep, st + ST_KEEP + wave * 256, row0 * (uint32_t)(p.keep_w * 4) + okeep, after);
     }
   };
   // The loads of a stage are spread over the step in NSLOT groups, each placed
@@ -369,8 +384,15 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
           uint32_t kbits = 0xF;
-          if (DROPOUT)
+          if (DROPOUT && KEEP) {
+            // Rows 8*cg + 4*g + u of the tile, this workgroup's word of this sub-block.
+            const unsigned char* kw = st + ST_KEEP + (qs * 32 + 8 * cg + 4 * g) * 16 + (kblk & 1) * 8 + sb * 4;
+            kbits = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kbits |= ((lds_at<uint32_t>(kw, u * 16) >> l32) & 1u) << u;
+          } else if (DROPOUT) {
             kbits = keep_bits_for_key(drop, bhg, p.Sq, sk4, q0 + 8 * cg + 4 * g, key, lane);
+          }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * cg + u;
@@ -427,11 +449,11 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
 __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
-  using C = BwdCfg<E, BIAS>;
+  using C = BwdCfg<E, BIAS, KEEP>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
-  constexpr int ST_K = 0, ST_V = 2 * TILE_B, ST_BIAS = 4 * TILE_B;
+  constexpr int ST_K = 0, ST_V = 2 * TILE_B, ST_BIAS = 4 * TILE_B, ST_KEEP = ST_BIAS + C::BIAS_B;
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int qsb = wave & 1, ks = wave >> 1;
@@ -459,6 +481,14 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int kt_end = CAUSAL ? min(nkt, min(q0b + 63, p.Sq - 1) / 32 + 1) : nkt;
   const int n_it = (kt_end + 1) / 2;
 
+  // Keep bits from the forward: stage it holds, for each of this workgroup's 64
+  // rows, the 16-byte chunk of words that contains the stage's two 32-key words.
+  __amdgpu_buffer_rsrc_t rkeep = make_rsrc(p.q, 0u);
+  uint32_t okeep = 0u;
+  if (KEEP) {
+    rkeep = make_rsrc(p.keep + (int64_t)bh * p.Sq * p.keep_w, (uint32_t)(p.Sq * p.keep_w * 4));
+    okeep = (uint32_t)((q0b + wave * 16 + (lane & 15)) * p.keep_w * 4);
+  }
   // Additive bias: stage it also holds the bias block of this workgroup's 64
   // rows x the stage's 64 keys; a lane reads keys 8*cg + 4*g + 0..3 of its
   // row (8 bytes) for register group cg.
@@ -482,10 +512,15 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   // tiles, then the two loads of the bias block.
   auto issue_one = [&](int it, int idx, float after) {
     unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
-    if (idx >= 4 * NLD) {
+    if (BIAS && idx >= 4 * NLD && idx < 4 * NLD + C::NBL) {
       const int k = idx - 4 * NLD;
       dma16_after(br, st + ST_BIAS + k * 4096 + wave * 1024, (uint32_t)(128 * it) + obias[k],
                   after);
+      return;
+    }
+    if (idx >= 4 * NLD) {
+      if (lane < 16)
+        dma16_after(rkeep, st + ST_KEEP + wave * 256, (uint32_t)((it >> 1) * 16) + okeep, after);
       return;
     }
     const int half = idx / (2 * NLD), tensor = (idx / NLD) & 1, k = idx % NLD;
@@ -616,7 +651,10 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 #pragma unroll
         for (int cg = 0; cg < 4; ++cg) {
           uint32_t kbits = 0xF;
-          if (DROPOUT) {
+          if (DROPOUT && KEEP) {
+            kbits = (lds_at<uint32_t>(st, ST_KEEP + (qsb * 32 + l32) * 16 + (it & 1) * 8 + ks * 4) >>
+                     (8 * cg + 4 * g)) & 0xFu;
+          } else if (DROPOUT) {
             const PhiloxOut w = philox4x32_10(drow + (uint32_t)(k0 >> 2) + 2 * cg + g,
                                               drop.seed_lo, drop.seed_hi);
             kbits = (w.w[0] >= drop.threshold ? 1u : 0u) |
@@ -666,9 +704,9 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 
 // Workgroup order: per head, dK/dV and dQ blocks alternate, heaviest causal
 // blocks first; all blocks of a head sit on one XCD when the head count allows.
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E, BIAS>::LDS_B];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E, BIAS, KEEP>::LDS_B];
   const int bh_count = p.B * p.H;
   int bh, slot;
   if ((bh_count & 7) == 0) {
@@ -691,9 +729,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb)
     rank = slot - m;
   }
   if (dkdv)
-    role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16>(p, bh, rank, lds);
+    role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16, KEEP>(p, bh, rank, lds);
   else
-    role_dq<E, CAUSAL, DROPOUT, BIAS, F16>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
+    role_dq<E, CAUSAL, DROPOUT, BIAS, F16, KEEP>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
 // -D_i = -rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every
@@ -730,10 +768,19 @@ hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream
                      dim3(256), 0, stream, p);
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
-  auto go = [&](auto c, auto d, auto bias) {
+  auto go2 = [&](auto c, auto d, auto bias, auto keep) {
     hipLaunchKernelGGL((bwd_kernel<E, decltype(c)::value, decltype(d)::value,
-                                   decltype(bias)::value, F16>),
+                                   decltype(bias)::value, F16, decltype(keep)::value>),
                        grid, dim3(256), 0, stream, p, nkb, nqb);
+  };
+  auto go = [&](auto c, auto d, auto bias) {
+    if constexpr (decltype(d)::value) {
+      if (p.keep != nullptr) {
+        go2(c, d, bias, Flag<true>{});
+        return;
+      }
+    }
+    go2(c, d, bias, Flag<false>{});
   };
   auto with_bias = [&](auto c, auto d) {
     if (p.bias != nullptr)

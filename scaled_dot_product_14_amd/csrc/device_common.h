@@ -79,6 +79,12 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Bitwise or over the lane pair (l, l^32).
+__device__ __forceinline__ uint32_t pair_or(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] | r[1];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Raw buffer resource over `bytes` bytes at `base`: 16-byte loads at offsets at

@@ -317,16 +317,28 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 
       if (DROPOUT) {
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb) {
+          uint32_t bits = 0;  // keep bits of this lane's 16 keys of the block, at key % 32
 #pragma unroll
           for (int cg = 0; cg < 4; ++cg) {
             // keys k0 + 32*kb + 8*cg + 4*g + 0..3: one Philox group
             const uint32_t grp = (uint32_t)(k0 >> 2) + kb * 8 + cg * 2 + g;
             const PhiloxOut w = philox4x32_10(drow + grp, p.drop.seed_lo, p.drop.seed_hi);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (w.w[t] < p.drop.threshold) pb[2 * kb + (cg >> 1)][4 * (cg & 1) + t] = (__bf16)0.f;
+            for (int t = 0; t < 4; ++t) {
+              const bool keep = w.w[t] >= p.drop.threshold;
+              if (!keep) pb[2 * kb + (cg >> 1)][4 * (cg & 1) + t] = (__bf16)0.f;
+              bits |= (keep ? 1u : 0u) << (8 * cg + 4 * g + t);
+            }
           }
+          // Optionally keep the mask for the backward: the two lanes of a row
+          // hold complementary halves of the block's word.
+          if (p.keep != nullptr) {
+            const uint32_t word = pair_or(bits);
+            if (g == 0 && qrow < p.Sq)
+              p.keep[((int64_t)bh * p.Sq + qrow) * p.keep_w + ((k0 + 32 * kb) >> 5)] = word;
+          }
+        }
       }
 
 #pragma unroll

@@ -26,6 +26,8 @@ struct FwdParams {
   DropoutParams drop;
   const uint16_t* bias;  // additive bias [B, H, Sq, Sk] (bf16 bits, unit key stride), or null
   Strides sbias;         // its strides (0 for a broadcast dimension)
+  uint32_t* keep;        // dropout keep bits [B, H, Sq, keep_w] words to write, or null
+  int keep_w;            // words per row: ceil(Sk / 32) rounded up to a multiple of 4
 };
 
 struct BwdParams {
@@ -46,6 +48,8 @@ struct BwdParams {
   DropoutParams drop;
   const uint16_t* bias;  // as in FwdParams
   Strides sbias;
+  const uint32_t* keep;  // keep bits written by the forward, or null: regenerate
+  int keep_w;
 };
 
 struct MaskParams {
@@ -68,6 +72,8 @@ hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool
 hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, bool f16,
                       hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
+// Words per row of the keep-bit cache: bit j % 32 of word j / 32 is key j's bit.
+inline int keep_words(int64_t Sk) { return (int)(((Sk + 31) / 32 + 3) / 4 * 4); }
 hipError_t launch_mask(const MaskParams& p, hipStream_t stream);
 // One thread: used[0..1] = state[0..1], then state[1] += advance.
 hipError_t launch_rng_step(uint64_t* state, uint64_t* used, uint64_t advance,

@@ -156,6 +156,7 @@ struct Ext {
   uint64_t* rng_used = nullptr;
   const uint16_t* bias = nullptr;
   Strides sbias{0, 0, 0};
+  uint32_t* keep_bits = nullptr;
 };
 
 int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int dtype,
@@ -204,6 +205,11 @@ int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
       const int rc = check_bias(ext->bias, B, H, Sq, Sk, dtype, &e);
       if (rc) return rc;
     }
+    e.keep_bits = ext->keep_bits;
+    if (reinterpret_cast<uintptr_t>(e.keep_bits) % 16 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "keep_bits is not 16-byte aligned");
+    if (e.keep_bits != nullptr && Sq * keep_words(Sk) * 4 >= (int64_t(1) << 32))
+      return fail(SDPA_ERR_UNSUPPORTED, "keep_bits of one (batch, head) span 4 GiB or more");
   }
   *out = e;
   return SDPA_OK;
@@ -332,6 +338,8 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   p.drop = make_dropout(dropout_p, s0, o0, e.heads_total, e.head_offset, e.rng_used);
   p.bias = e.bias;
   p.sbias = e.sbias;
+  p.keep = drop ? e.keep_bits : nullptr;
+  p.keep_w = keep_words(dk.S);
   const hipError_t err = timed_launch(SDPA_KERNEL_FWD, st, [&] {
     return launch_fwd(p, (int)dq.E, is_causal != 0, drop, dq.dtype == SDPA_F16, tile_choice(),
                       st);
@@ -417,6 +425,8 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   p.drop = make_dropout(dropout_p, seed, offset, e.heads_total, e.head_offset, e.rng_used);
   p.bias = e.bias;
   p.sbias = e.sbias;
+  p.keep = dropout_p > 0.0 ? e.keep_bits : nullptr;
+  p.keep_w = keep_words(dki.S);
   const int E = (int)dqi.E;
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -427,6 +437,11 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
                                                           dqi.dtype == SDPA_F16, st);
                                       });
   return hip_status(err, "backward launch");
+}
+
+size_t sdpa_keep_bits_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
+  if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0) return 0;
+  return (size_t)B * (size_t)H * (size_t)Sq * (size_t)keep_words(Sk) * 4u;
 }
 
 size_t sdpa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq) {

@@ -279,3 +279,43 @@ def test_everything_together_fp16_sharded_device_rng_bias():
     assert_out(host64(out), ref_out[sl])
     assert_lse(lse.cpu().double().numpy(), ref_lse[sl])
     assert_grads([(n, host64(a), r[sl]) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,f16,with_bias", [
+    (4, 16, 1000, 1000, 64, "BHSE", True, False, False),
+    (2, 3, 200, 330, 64, "BSHE", False, False, False),
+    (1, 2, 130, 250, 128, "BHSE", False, True, True),
+    (2, 2, 256, 256, 128, "BHSE", True, False, False),
+])
+def test_keep_bit_cache(B, H, Sq, Sk, E, layout, causal, f16, with_bias):
+    say(f"keep-bit cache B{B} H{H} Sq{Sq} Sk{Sk} E{E} {layout} causal={causal} f16={f16} bias={with_bias}")
+    q, k, v, do = workloads.draw(B, H, Sq, Sk, E, 29, 1.0, layout, device="cuda")
+    if f16:
+        q, k, v, do = (workloads.to_layout(t.to(torch.float16), layout) for t in (q, k, v, do))
+    bias = None
+    if with_bias:
+        pad = (Sk + 7) // 8 * 8
+        g = torch.Generator("cpu").manual_seed(30)
+        bias = torch.randn((1, H, Sq, pad), generator=g).to(q.dtype).to("cuda")[..., :Sk]
+    p, seed, off = 0.2, 808, 96
+    kb = torch.empty(sdpa.sdpa_keep_bits_size(B, H, Sq, Sk) // 4, dtype=torch.int32, device="cuda")
+    sdpa.sdpa_set_rng_state(seed, off)
+    o1, l1, s, f = sdpa.sdpa_fwd_ext(q, k, v, p, causal, bias=bias, keep_bits=kb)
+    g1 = sdpa.sdpa_bwd_ext(do, q, k, v, o1, l1, p, causal, s, f, bias=bias, keep_bits=kb)
+    sdpa.sdpa_set_rng_state(seed, off)
+    o2, l2, s, f = sdpa.sdpa_fwd_ext(q, k, v, p, causal, bias=bias)
+    g2 = sdpa.sdpa_bwd_ext(do, q, k, v, o2, l2, p, causal, s, f, bias=bias)
+    mask = sdpa.sdpa_debug_dropout_mask(seed, off, p, B, H, Sq, Sk)
+    torch.cuda.synchronize()
+    # Outputs and gradients are the same computation with the same mask.
+    for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
+        assert torch.equal(a, b)
+    # The cached bits are the mask, wherever a row can see the key.
+    W = kb.numel() // (B * H * Sq)
+    words = kb.view(B, H, Sq, W).to(torch.int64) & 0xFFFFFFFF
+    j = torch.arange(Sk, device="cuda")
+    bits = (words[..., j // 32] >> (j % 32)) & 1
+    visible = torch.ones(Sq, Sk, dtype=torch.bool, device="cuda")
+    if causal:
+        visible = visible.tril()
+    assert torch.equal(bits.to(torch.uint8)[..., visible], mask[..., visible])

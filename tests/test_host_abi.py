@@ -252,3 +252,23 @@ def test_size_one_dims_ignore_strides(lib):
     q = _t(B=1, stride=(3, 128 * 64, 64, 1))
     rc = _fwd(lib, q=q, p=2.0)
     assert rc == bnd.SDPA_ERR_INVALID and "dropout" in _err(lib)
+
+
+def test_keep_bits_size():
+    assert bnd.sdpa_keep_bits_size(2, 3, 5, 1000) == 2 * 3 * 5 * 32 * 4  # ceil(1000/32)=32 words
+    assert bnd.sdpa_keep_bits_size(1, 1, 1, 33) == 4 * 4                # 2 words -> 4
+    assert bnd.sdpa_keep_bits_size(1, 1, 1, 129) == 8 * 4               # 5 words -> 8
+    assert bnd.sdpa_keep_bits_size(0, 1, 1, 1) == 0
+
+
+def test_keep_bits_alignment_checked(lib):
+    bnd.sdpa_set_rng_state(61, 62)
+    ext = _ext()
+    ext.keep_bits = FAKE + 8
+    q, k, v, out = _t(), _t(), _t(), _t()
+    s, o = ctypes.c_uint64(), ctypes.c_uint64()
+    rc = lib.sdpa_fwd_ext(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0.1, 1, math.nan,
+                          ctypes.byref(out), FAKE, ctypes.byref(s), ctypes.byref(o),
+                          ctypes.byref(ext), None)
+    assert rc == bnd.SDPA_ERR_UNSUPPORTED and "keep_bits" in _err(lib)
+    assert bnd.sdpa_get_rng_state() == (61, 62)
