@@ -36,6 +36,9 @@
 // per visible score element (5 are counted).  In exchange dQ needs neither
 // fp32 atomics nor a zeroed accumulator nor a conversion pass, and every output
 // is bitwise reproducible.
+#include <algorithm>
+#include <vector>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_ring.h"
@@ -702,10 +705,20 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   exchange_finish<E, F16>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, red, 2 * qsb + (1 - ks), upper, lane);
 }
 
-// Workgroup order: per head, dK/dV and dQ blocks alternate, heaviest causal
-// blocks first; all blocks of a head sit on one XCD when the head count allows.
+// Order in which a head's dK/dV and dQ blocks are dealt out: longest estimated
+// run first, so the short blocks fill in at the end (longest-processing-time
+// first).  Entry s: bit 15 set for a dQ block, low bits the block's rank.
+constexpr int kMaxOrder = 1024;
+struct BwdOrder {
+  uint16_t item[kMaxOrder];
+};
+
+// Workgroup order: per head, blocks in BwdOrder order (or, past kMaxOrder
+// blocks, dK/dV and dQ alternating, heaviest causal blocks first); all blocks
+// of a head sit on one XCD when the head count allows.
 template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb) {
+__global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb, BwdOrder ord,
+                                                  int use_order) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E, BIAS, KEEP>::LDS_B];
   const int bh_count = p.B * p.H;
   int bh, slot;
@@ -718,15 +731,21 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb)
     slot = blockIdx.x / bh_count;
     bh = blockIdx.x - slot * bh_count;
   }
-  const int m = min(nkb, nqb);
   bool dkdv;
   int rank;
-  if (slot < 2 * m) {
-    dkdv = (slot & 1) == 0;
-    rank = slot >> 1;
+  if (use_order) {
+    const int e = ord.item[slot];
+    dkdv = (e & 0x8000) == 0;
+    rank = e & 0x7FFF;
   } else {
-    dkdv = nkb > nqb;
-    rank = slot - m;
+    const int m = min(nkb, nqb);
+    if (slot < 2 * m) {
+      dkdv = (slot & 1) == 0;
+      rank = slot >> 1;
+    } else {
+      dkdv = nkb > nqb;
+      rank = slot - m;
+    }
   }
   if (dkdv)
     role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16, KEEP>(p, bh, rank, lds);
@@ -768,10 +787,35 @@ hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream
                      dim3(256), 0, stream, p);
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
+  BwdOrder ord;
+  const int use_order = nkb + nqb <= kMaxOrder ? 1 : 0;
+  if (use_order) {
+    // Estimated run of a block: steps times a measured per-step cost plus a
+    // fixed prologue/epilogue (dK/dV: ~1.5 us per step + ~4 us; dQ: ~1.1 us +
+    // ~3.3 us, at b2 h12 s1024 d64), in units of 0.1 us.
+    const int nqt = (p.Sq + 31) / 32, nkt = (p.Sk + 31) / 32;
+    struct Item {
+      int cost, key;
+    };
+    std::vector<Item> items;
+    items.reserve(nkb + nqb);
+    for (int r = 0; r < nkb; ++r) {
+      const int t0 = causal ? std::min(2 * r, nqt) : 0;
+      items.push_back({15 * ((nqt - t0 + 1) / 2) + 40, r});
+    }
+    for (int r = 0; r < nqb; ++r) {
+      const int qblk = causal ? nqb - 1 - r : r;
+      const int kt_end = causal ? std::min(nkt, std::min(64 * qblk + 63, p.Sq - 1) / 32 + 1) : nkt;
+      items.push_back({11 * ((kt_end + 1) / 2) + 33, 0x8000 | r});
+    }
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& a, const Item& b) { return a.cost > b.cost; });
+    for (size_t i = 0; i < items.size(); ++i) ord.item[i] = (uint16_t)items[i].key;
+  }
   auto go2 = [&](auto c, auto d, auto bias, auto keep) {
     hipLaunchKernelGGL((bwd_kernel<E, decltype(c)::value, decltype(d)::value,
                                    decltype(bias)::value, F16, decltype(keep)::value>),
-                       grid, dim3(256), 0, stream, p, nkb, nqb);
+                       grid, dim3(256), 0, stream, p, nkb, nqb, ord, use_order);
   };
   auto go = [&](auto c, auto d, auto bias) {
     if constexpr (decltype(d)::value) {
