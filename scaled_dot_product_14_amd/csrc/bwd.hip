@@ -315,10 +315,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                    (uint32_t)(p.sv.s * 2), ovv);
   }
   if (n_it > 0) issue(0);
-  if (n_it > 1) issue(1);
-  if (n_it > 1)
-    ring_barrier<2 * C::NPAIR_A>();
-  else if (n_it > 0)
+  // The block's own tiles first; stage 1 goes out once they are in.
+  if (n_it > 0)
     ring_barrier<C::NPAIR_A>();
   else
     ring_barrier<0>();
@@ -328,6 +326,7 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     kf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_A + sb * TILE_B, aoff[es]);
     vf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_A + (2 + sb) * TILE_B, aoff[es]);
   }
+  if (n_it > 1) issue(1);
   if (n_it > 1)
     ring_barrier<C::NPAIR_A>();
   else
@@ -583,10 +582,8 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
             (uint32_t)q0b * 4u + (uint32_t)((wave & 1) * 128 + lane * 16));
   }
   if (n_it > 0) issue(0);
-  if (n_it > 1) issue(1);
-  if (n_it > 1)
-    ring_barrier<2 * C::NPAIR_B>();
-  else if (n_it > 0)
+  // The block's own tiles first; stage 1 goes out once they are in.
+  if (n_it > 0)
     ring_barrier<C::NPAIR_B>();
   else
     ring_barrier<0>();
@@ -602,6 +599,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   f32x16 dinit;
 #pragma unroll
   for (int r = 0; r < 16; ++r) dinit[r] = DROPOUT ? 0.f : ndsum;
+  if (n_it > 1) issue(1);
   if (n_it > 1)
     ring_barrier<C::NPAIR_B>();
   else
