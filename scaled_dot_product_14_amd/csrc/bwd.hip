@@ -752,37 +752,46 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb,
 }
 
 // -D_i = -rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every
-// row, in two planes of B*H*Sq floats.  CPR lanes share a row; each loads one
+// row, in two planes of B*H*Sq floats.  A block covers RPB rows of one head
+// (block v of `total` is row block v % nblk of head v / nblk, so all index
+// arithmetic is 32-bit and uniform); CPR lanes share a row and each loads one
 // 16-byte chunk of dO and of O.
 template <int E, bool F16>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, uint32_t nblk,
+                                                        uint32_t total) {
   constexpr int CPR = E / 8, RPB = 256 / CPR;
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / CPR;
   const int col = tid % CPR;
+  const float log2_scale = __log2f(p.scale);
   const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  float d = 0.f;
-  if (row < rows) {
-    const int64_t bh = row / p.Sq;
-    const int64_t i = row - bh * p.Sq;
-    const int64_t b = bh / p.H, h = bh - (bh / p.H) * p.H;
-    const bf16x8 x = load_bf16x8(p.dout + b * p.sdo.b + h * p.sdo.h + i * p.sdo.s + col * 8);
-    const bf16x8 y = load_bf16x8(p.o + b * p.so.b + h * p.so.h + i * p.so.s + col * 8);
-    d = dot8_16<F16>(x, y, 0.f);
-  }
-  d = group_sum<CPR>(d);
-  if (row < rows && col == 0) {
-    p.dl[row] = -d;
-    p.dl[rows + row] = p.lse[row] * kLog2e - __log2f(p.scale);
+  for (uint64_t vv = blockIdx.x; vv < total; vv += gridDim.x) {
+    const uint32_t v = (uint32_t)vv;
+    const uint32_t bh = v / nblk;
+    const int i = (int)(v - bh * nblk) * RPB + tid / CPR;
+    const uint32_t b = bh / (uint32_t)p.H, h = bh - b * (uint32_t)p.H;
+    float d = 0.f;
+    if (i < p.Sq) {
+      const bf16x8 x = load_bf16x8(p.dout + b * p.sdo.b + h * p.sdo.h + i * p.sdo.s + col * 8);
+      const bf16x8 y = load_bf16x8(p.o + b * p.so.b + h * p.so.h + i * p.so.s + col * 8);
+      d = dot8_16<F16>(x, y, 0.f);
+    }
+    d = group_sum<CPR>(d);
+    if (i < p.Sq && col == 0) {
+      const int64_t row = (int64_t)bh * p.Sq + i;
+      p.dl[row] = -d;
+      p.dl[rows + row] = p.lse[row] * kLog2e - log2_scale;
+    }
   }
 }
 
 template <int E, bool F16>
 hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
   constexpr int RPB = 256 / (E / 8);
-  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  hipLaunchKernelGGL((bwd_prep_kernel<E, F16>), dim3((unsigned)((rows + RPB - 1) / RPB)),
-                     dim3(256), 0, stream, p);
+  // B*H*nblk < 2^32: B*H*ceil(Sq/32) is below 2^31 and RPB >= 16.
+  const uint32_t nblk = (uint32_t)((p.Sq + RPB - 1) / RPB);
+  const uint32_t total = (uint32_t)((int64_t)p.B * p.H * nblk);
+  hipLaunchKernelGGL((bwd_prep_kernel<E, F16>), dim3(std::min(total, 1u << 20)), dim3(256), 0,
+                     stream, p, nblk, total);
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
   BwdOrder ord;

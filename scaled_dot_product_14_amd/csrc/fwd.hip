@@ -216,11 +216,14 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
     drow = philox_row_base(p.drop, dropout_head(p.drop, b, h), p.Sq, qrow, sk4);
   }
 
-  const int npre = min(n_it, NSTAGE - 1);
-  for (int it = 0; it < npre; ++it) issue(it);
+  // Stage 0 goes out with Q; with three stages, stage 1 follows once both are
+  // in, so the start-up burst of every workgroup carries only what its first
+  // step needs.
+  if (n_it > 0) issue(0);
 #pragma unroll
-  for (int es = 0; es < NES; ++es) settle(qf[es]);  // waits for the stages too
+  for (int es = 0; es < NES; ++es) settle(qf[es]);  // waits for stage 0 too
   ring_barrier<0>();
+  if (NSTAGE == 3 && n_it > 1) issue(1);
 
   for (int it = 0; it < n_it; ++it) {
     const int j = it * NS + ksp;
