@@ -258,13 +258,12 @@ int hip_status(hipError_t err, const char* what) {
   return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
+// The forward workgroup shape is chosen per problem; SDPA14_FWD_SHAPE (1, 2
+// or 3) forces one, read on every call so that a process can compare them.
 TileChoice tile_choice() {
-  static const TileChoice tc = [] {
-    TileChoice t{0};
-    if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
-    return t;
-  }();
-  return tc;
+  TileChoice t{0};
+  if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
+  return t;
 }
 
 }  // namespace
