@@ -38,7 +38,13 @@
 //
 // Workgroup order: heaviest causal query tiles first, and the tiles of one head
 // on one XCD (workgroups are dealt to the 8 XCDs round-robin), so a head's K/V
-// stay in that XCD's L2.
+// stay in that XCD's L2.  When the whole grid is resident at once, every
+// workgroup asks for its Q and first K/V stage at the same moment; a light
+// causal tile then waits a little before its first loads (longer the fewer
+// steps it has), so that the heaviest tiles, which set the kernel's length,
+// are served first.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_ring.h"
@@ -74,7 +80,7 @@ __device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& 
 }
 
 template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
-__global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles) {
+__global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles, int hold) {
   static_assert(E % 64 == 0 && BN % 32 == 0, "tile shape");
   constexpr int NW = NQ * NS;
   constexpr int NT = NW * 64;
@@ -124,6 +130,15 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   if (CAUSAL) kend = min(kend, min(p.Sq, (qt + 1) * BM));  // keys <= last row of the tile
   const int n_kt = (kend + BN - 1) / BN;
   const int n_it = (n_kt + NS - 1) / NS;
+
+  // Start-up hold: up to `hold` sleeps of ~640 clocks, one per step this tile
+  // has fewer than the heaviest one.
+  if (CAUSAL && hold > 0) {
+    const int kend_max = min(p.Sk, min(p.Sq, n_qtiles * BM));
+    const int n_it_max = ((kend_max + BN - 1) / BN + NS - 1) / NS;
+    const int units = min(n_it_max - n_it, hold);
+    for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(10);
+  }
 
   // Q as the B operand of S^T = K Q^T: lane holds its row, e = 16*es + 8*g + 0..7.
   // Rows past Sq read as zeros through the buffer range check.
@@ -412,6 +427,34 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   }
 }
 
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Workgroups of kernel K resident per compute unit (queried once per kernel).
+template <auto K>
+int resident_per_cu(int threads) {
+  static std::atomic<int> cache{-1};
+  int n = cache.load(std::memory_order_relaxed);
+  if (n < 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, K, threads, 0) != hipSuccess) n = 0;
+    cache.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+constexpr int kHoldSteps = 4;  // longest start-up hold, in steps of slack
+
 template <int E, int NQ, int NS, int BN>
 hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, bool f16,
                         hipStream_t stream) {
@@ -420,9 +463,12 @@ hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, bool f16,
   const dim3 grid((unsigned)n_qtiles * (unsigned)(p.B * p.H));
   const dim3 block(NQ * NS * 64);
   auto go2 = [&](auto c, auto d, auto bias, auto half) {
-    hipLaunchKernelGGL((fwd_kernel<E, NQ, NS, BN, decltype(c)::value, decltype(d)::value,
-                                   decltype(bias)::value, decltype(half)::value>),
-                       grid, block, 0, stream, p, n_qtiles);
+    constexpr auto kernel = &fwd_kernel<E, NQ, NS, BN, decltype(c)::value, decltype(d)::value,
+                                        decltype(bias)::value, decltype(half)::value>;
+    // Hold light tiles back only when the whole grid runs in one round.
+    const long slots = (long)device_cus() * resident_per_cu<kernel>((int)block.x);
+    const int hold = (decltype(c)::value && (long)grid.x <= slots) ? kHoldSteps : 0;
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, p, n_qtiles, hold);
   };
   auto go = [&](auto c, auto d, auto bias) {
     if (f16)
