@@ -502,10 +502,18 @@ hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool
   // Shape: 4 query sub-tiles sharing each key tile when there are enough
   // 128-row tiles to give every compute unit two workgroups; otherwise two
   // query sub-tiles with the keys split in two, for a shorter critical path.
+  // When even 32-row tiles leave a compute unit per workgroup (head dim 64,
+  // e.g. a few heads of one GPU's share) and there are keys for four shares,
+  // one sub-tile with the keys split in four: its 128 KB of LDS then costs no
+  // concurrency.
   int shape = tiles.fwd_shape;  // 1: NQ=4,NS=1   2: NQ=2,NS=2   3: NQ=1,NS=4
   if (shape < 1 || shape > 3) {
     const long wg4 = (long)((p.Sq + 127) / 128) * p.B * p.H;
-    shape = (wg4 >= 512) ? 1 : 2;
+    const long wg1 = (long)((p.Sq + 31) / 32) * p.B * p.H;
+    if (E == 64 && p.Sk >= 4 * 64 && wg1 <= device_cus())
+      shape = 3;
+    else
+      shape = (wg4 >= 512) ? 1 : 2;
   }
   if (E == 64) {
     if (shape == 1) return launch_fwd_t<64, 4, 1, 64>(p, causal, dropout, f16, stream);

@@ -92,6 +92,11 @@ EXTRA = [
     (2, 2, 257, 129, 64, "BSHE", False, 0.3, 17),
     (1, 2, 200, 333, 64, "BSHE", True, 0.0, 18),
     (3, 5, 64, 64, 64, "BHSE", True, 0.5, 19),
+    # Grids small enough for one 32-row workgroup per compute unit take the
+    # four-key-share forward by default: one GPU's share of the 2x12x1024
+    # problem with dropout, and a non-causal BSHE case with Sq < Sk.
+    (2, 3, 1024, 1024, 64, "BHSE", True, 0.1, 20),
+    (1, 4, 512, 2048, 64, "BSHE", False, 0.0, 21),
 ]
 
 
