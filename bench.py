@@ -185,7 +185,7 @@ def cpu_baseline(w, q, k, v, do, min_seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
               "multi-GPU path: heads shard across GPUs with no exchange, so one GPU's share is "
               "the same kernel on fewer heads.", file=sys.stderr)
         sys.exit(2)

@@ -63,7 +63,7 @@ typedef struct ihipStream_t* sdpa_stream_t;
 typedef enum sdpa_status {
   SDPA_OK = 0,
   SDPA_ERR_INVALID = 1,     /* null pointer, shape mismatch, E != Ev, p not in [0,1), bad scale */
-  SDPA_ERR_UNSUPPORTED = 2, /* dtype, head dim, stride or alignment this build does not handle */
+  SDPA_ERR_UNSUPPORTED = 2, /* dtype, head dim, stride or alignment the kernels do not handle */
   SDPA_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or smaller than required */
   SDPA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } sdpa_status;
