@@ -79,32 +79,45 @@ __device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& 
   }
 }
 
-template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
-__global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles, int hold) {
+// Tile geometry and LDS layout of a workgroup of NQ x NS waves with key tiles
+// of BN rows per share.
+template <int E, int NQ, int NS, int BN, bool BIAS>
+struct FwdGeom {
   static_assert(E % 64 == 0 && BN % 32 == 0, "tile shape");
-  constexpr int NW = NQ * NS;
-  constexpr int NT = NW * 64;
-  constexpr int BM = NQ * 32;
-  constexpr int NES = E / 16;
-  constexpr int NEB = E / 32;
-  constexpr int ROWS = NS * BN;         // key rows staged per iteration
-  constexpr int ROW_B = 2 * E;
-  constexpr int KT_B = ROWS * ROW_B;    // bytes of the K (and of the V) rows of a stage
-  constexpr int STAGE = 2 * KT_B;       // [K rows][V rows], swizzled, unpadded
-  constexpr int NSTAGE = (3 * STAGE <= 64 * 1024) ? 3 : 2;  // keep two workgroups per CU
+  static constexpr int NW = NQ * NS;
+  static constexpr int NT = NW * 64;
+  static constexpr int BM = NQ * 32;
+  static constexpr int ROWS = NS * BN;       // key rows staged per iteration
+  static constexpr int ROW_B = 2 * E;
+  static constexpr int KT_B = ROWS * ROW_B;  // bytes of the K (and of the V) rows of a stage
+  static constexpr int STAGE = 2 * KT_B;     // [K rows][V rows], swizzled, unpadded
+  static constexpr int NSTAGE = (3 * STAGE <= 64 * 1024) ? 3 : 2;  // keep two workgroups per CU
   static_assert(KT_B % (NT * 16) == 0, "whole loads per thread");
-  constexpr int NLD = KT_B / (NT * 16);  // loads per thread per tensor per stage
-  constexpr int NPS = 2 * NLD;           // loads per thread per stage
-  constexpr int CMB_FLOATS = (NS - 1) * NQ * (NEB * 16 + 2) * 64;  // merge buffer
+  static constexpr int NLD = KT_B / (NT * 16);  // loads per thread per tensor per stage
+  static constexpr int CMB_FLOATS = (NS - 1) * NQ * (E / 32 * 16 + 2) * 64;  // merge buffer
   // Per-wave bias scratch after the ring: 32 rows x 32 keys, rows padded to
   // 72 bytes (8-byte aligned, at most two lanes of a 32-lane read per bank).
-  constexpr int BS_ROW_B = 72;
-  constexpr int BS_WAVE_B = 32 * BS_ROW_B;
-  constexpr int BS_OFF = NSTAGE * STAGE;
-  constexpr int RING_AND_BIAS = BS_OFF + (BIAS ? NW * BS_WAVE_B : 0);
-  constexpr int LDS_BYTES = RING_AND_BIAS > CMB_FLOATS * 4 ? RING_AND_BIAS : CMB_FLOATS * 4;
+  static constexpr int BS_ROW_B = 72;
+  static constexpr int BS_WAVE_B = 32 * BS_ROW_B;
+  static constexpr int BS_OFF = NSTAGE * STAGE;
+  static constexpr int RING_AND_BIAS = BS_OFF + (BIAS ? NW * BS_WAVE_B : 0);
+  static constexpr int LDS_BYTES =
+      RING_AND_BIAS > CMB_FLOATS * 4 ? RING_AND_BIAS : CMB_FLOATS * 4;
+};
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+// One workgroup's query tile qt (BM rows) of head bh.  n_it_max: steps of the
+// heaviest tile of its kind, for the start-up hold.
+template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
+__device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int n_it_max,
+                                         int hold, unsigned char* lds) {
+  using G = FwdGeom<E, NQ, NS, BN, BIAS>;
+  constexpr int NW = G::NW, NT = G::NT, BM = G::BM;
+  constexpr int NES = E / 16;
+  constexpr int NEB = E / 32;
+  constexpr int ROWS = G::ROWS, ROW_B = G::ROW_B, KT_B = G::KT_B, STAGE = G::STAGE;
+  constexpr int NSTAGE = G::NSTAGE, NLD = G::NLD;
+  constexpr int NPS = 2 * NLD;  // loads per thread per stage
+  constexpr int BS_ROW_B = G::BS_ROW_B, BS_WAVE_B = G::BS_WAVE_B, BS_OFF = G::BS_OFF;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -114,9 +127,6 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   const int qs = wave % NQ;   // query sub-tile of this wave
   const int ksp = wave / NQ;  // key share of this wave
 
-  int bh, rank;
-  wg_to_tile(blockIdx.x, p.B * p.H, bh, rank);
-  const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int q0 = qt * BM + qs * 32;  // first query row of this wave
@@ -134,8 +144,6 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   // Start-up hold: up to `hold` sleeps of ~640 clocks, one per step this tile
   // has fewer than the heaviest one.
   if (CAUSAL && hold > 0) {
-    const int kend_max = min(p.Sk, min(p.Sq, n_qtiles * BM));
-    const int n_it_max = ((kend_max + BN - 1) / BN + NS - 1) / NS;
     const int units = min(n_it_max - n_it, hold);
     for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(10);
   }
@@ -226,9 +234,10 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 
   const int sk4 = (p.Sk + 3) >> 2;
   uint64_t drow = 0;
+  DropoutParams drop = p.drop;  // the device-resident RNG state, when used, is read into this copy
   if (DROPOUT) {
-    load_dropout_state(p.drop);
-    drow = philox_row_base(p.drop, dropout_head(p.drop, b, h), p.Sq, qrow, sk4);
+    load_dropout_state(drop);
+    drow = philox_row_base(drop, dropout_head(drop, b, h), p.Sq, qrow, sk4);
   }
 
   // Stage 0 goes out with Q; with three stages, stage 1 follows once both are
@@ -341,10 +350,10 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
           for (int cg = 0; cg < 4; ++cg) {
             // keys k0 + 32*kb + 8*cg + 4*g + 0..3: one Philox group
             const uint32_t grp = (uint32_t)(k0 >> 2) + kb * 8 + cg * 2 + g;
-            const PhiloxOut w = philox4x32_10(drow + grp, p.drop.seed_lo, p.drop.seed_hi);
+            const PhiloxOut w = philox4x32_10(drow + grp, drop.seed_lo, drop.seed_hi);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              const bool keep = w.w[t] >= p.drop.threshold;
+              const bool keep = w.w[t] >= drop.threshold;
               if (!keep) pb[2 * kb + (cg >> 1)][4 * (cg & 1) + t] = (__bf16)0.f;
               bits |= (keep ? 1u : 0u) << (8 * cg + 4 * g + t);
             }
@@ -411,7 +420,7 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
   }
 
   const float l_tot = pair_sum(l_run);
-  const float inv = (DROPOUT ? p.drop.keep_scale : 1.f) / l_tot;
+  const float inv = (DROPOUT ? drop.keep_scale : 1.f) / l_tot;
   if (qrow < p.Sq) {
     uint16_t* op = p.o + b * p.so.b + h * p.so.h + (int64_t)qrow * p.so.s;
 #pragma unroll
@@ -424,6 +433,56 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
                         oacc[eb][4 * cg + 2] * inv, oacc[eb][4 * cg + 3] * inv);
       }
     if (g == 0 && p.lse != nullptr) p.lse[(int64_t)bh * p.Sq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// Steps of the heaviest causal tile of BM rows, key tiles of BN rows dealt to
+// NS shares, among query rows below `rows`.
+__device__ __forceinline__ int causal_steps_max(const FwdParams& p, int rows, int BN, int NS) {
+  const int kend = min(p.Sk, min(p.Sq, rows));
+  return ((kend + BN - 1) / BN + NS - 1) / NS;
+}
+
+template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16>
+__global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles, int hold) {
+  using G = FwdGeom<E, NQ, NS, BN, BIAS>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
+  int bh, rank;
+  wg_to_tile(blockIdx.x, p.B * p.H, bh, rank);
+  const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+  const int n_it_max = CAUSAL ? causal_steps_max(p, n_qtiles * G::BM, BN, NS) : 0;
+  fwd_tile<E, NQ, NS, BN, CAUSAL, DROPOUT, BIAS, F16>(p, bh, qt, n_it_max, hold, lds);
+}
+
+// Causal forward with two workgroup kinds in one launch.  The last rows of
+// each head, whose tiles see the most keys, go to 32-row workgroups with the
+// keys dealt to four waves in 32-key tiles; the rows before them to 64-row
+// workgroups of two sub-tiles x two shares of 64-key tiles.  Both kinds use 64
+// KB of LDS, so two workgroups share a compute unit whatever their kind, and
+// the longest chain of steps of a head is cut where it starts to dominate.
+// Workgroups 0 .. n_heavy*B*H-1 are the 32-row tiles, heaviest first; the
+// 64-row tiles follow, heaviest first; each kind keeps a head on one XCD.
+template <int E, bool DROPOUT, bool BIAS, bool F16>
+__global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy, int n_light,
+                                                        int hold) {
+  using GH = FwdGeom<E, 1, 4, 32, BIAS>;
+  using GL = FwdGeom<E, 2, 2, 64, BIAS>;
+  constexpr int LDS_B = GH::LDS_BYTES > GL::LDS_BYTES ? GH::LDS_BYTES : GL::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_B];
+  const int bh_count = p.B * p.H;
+  const int light_rows = n_light * 64;
+  const int nh = n_heavy * bh_count;
+  int bh, rank;
+  if ((int)blockIdx.x < nh) {
+    wg_to_tile(blockIdx.x, bh_count, bh, rank);
+    const int qt = light_rows / 32 + (n_heavy - 1 - rank);
+    fwd_tile<E, 1, 4, 32, true, DROPOUT, BIAS, F16>(
+        p, bh, qt, causal_steps_max(p, light_rows + 32 * n_heavy, 32, 4), hold, lds);
+  } else {
+    wg_to_tile((int)blockIdx.x - nh, bh_count, bh, rank);
+    const int qt = n_light - 1 - rank;
+    fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16>(p, bh, qt, causal_steps_max(p, light_rows, 64, 2),
+                                                    hold, lds);
   }
 }
 
@@ -495,6 +554,52 @@ hipError_t launch_fwd_t(const FwdParams& p, bool causal, bool dropout, bool f16,
   return hipGetLastError();
 }
 
+// Rows of each head that go to the 32-row, four-share kind of the split
+// forward: the last 256, the rest rounded to whole 64-row tiles.
+struct SplitRows {
+  int n_light, n_heavy;
+};
+inline SplitRows split_rows(int Sq) {
+  const int light_rows = Sq > 256 ? (Sq - 256) / 64 * 64 : 0;
+  return {light_rows / 64, (Sq - light_rows + 31) / 32};
+}
+
+template <int E>
+hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, hipStream_t stream) {
+  const SplitRows r = split_rows(p.Sq);
+  const dim3 grid((unsigned)(r.n_light + r.n_heavy) * (unsigned)(p.B * p.H));
+  auto go = [&](auto d, auto bias, auto half) {
+    constexpr auto kernel = &fwd_split_kernel<E, decltype(d)::value, decltype(bias)::value,
+                                              decltype(half)::value>;
+    const long slots = (long)device_cus() * resident_per_cu<kernel>(256);
+    const int hold = ((long)grid.x <= slots) ? kHoldSteps : 0;
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light, hold);
+  };
+  auto with_half = [&](auto d, auto bias) {
+    if (f16)
+      go(d, bias, Flag<true>{});
+    else
+      go(d, bias, Flag<false>{});
+  };
+  auto with_bias = [&](auto d) {
+    if (p.bias != nullptr)
+      with_half(d, Flag<true>{});
+    else
+      with_half(d, Flag<false>{});
+  };
+  if (dropout)
+    with_bias(Flag<true>{});
+  else
+    with_bias(Flag<false>{});
+  return hipGetLastError();
+}
+
+// Whole grid of the split forward resident at once (two workgroups per CU).
+bool split_fits(const FwdParams& p) {
+  const SplitRows r = split_rows(p.Sq);
+  return (long)(r.n_light + r.n_heavy) * p.B * p.H <= 2L * device_cus();
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool f16,
@@ -506,15 +611,24 @@ hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool
   // e.g. a few heads of one GPU's share) and there are keys for four shares,
   // one sub-tile with the keys split in four: its 128 KB of LDS then costs no
   // concurrency.
-  int shape = tiles.fwd_shape;  // 1: NQ=4,NS=1   2: NQ=2,NS=2   3: NQ=1,NS=4
-  if (shape < 1 || shape > 3) {
+  // A causal problem that would take two by two, with at least 512 rows and a
+  // grid that fits the chip at once, takes the split launch (4): its last 256
+  // rows per head in 32-row, four-share workgroups.
+  int shape = tiles.fwd_shape;  // 1: NQ=4,NS=1   2: NQ=2,NS=2   3: NQ=1,NS=4   4: split
+  if (shape < 1 || shape > 4) {
     const long wg4 = (long)((p.Sq + 127) / 128) * p.B * p.H;
     const long wg1 = (long)((p.Sq + 31) / 32) * p.B * p.H;
     if (E == 64 && p.Sk >= 4 * 64 && wg1 <= device_cus())
       shape = 3;
+    else if (wg4 >= 512)
+      shape = 1;
+    else if (E == 64 && causal && p.Sq >= 512 && split_fits(p))
+      shape = 4;
     else
-      shape = (wg4 >= 512) ? 1 : 2;
+      shape = 2;
   }
+  if (shape == 4 && (E != 64 || !causal)) shape = 2;  // the split launch is causal, head dim 64
+  if (shape == 4) return launch_fwd_split<64>(p, dropout, f16, stream);
   if (E == 64) {
     if (shape == 1) return launch_fwd_t<64, 4, 1, 64>(p, causal, dropout, f16, stream);
     if (shape == 2) return launch_fwd_t<64, 2, 2, 64>(p, causal, dropout, f16, stream);

@@ -61,7 +61,8 @@ struct MaskParams {
 // Tile choices the launchers take; 0 lets the launcher decide.
 struct TileChoice {
   int fwd_shape;  // forward workgroup: 1 = 4 query sub-tiles, 2 = 2 sub-tiles x 2 key
-                  // shares, 3 = 1 sub-tile x 4 key shares (32 query rows per sub-tile)
+                  // shares, 3 = 1 sub-tile x 4 key shares (32 query rows per sub-tile),
+                  // 4 = causal split launch (kinds 3 with 32-key tiles and 2, head dim 64)
 };
 
 // f16: the 16-bit tensors are IEEE half instead of bfloat16.

@@ -1,12 +1,15 @@
 """GPU parity of every forward workgroup shape against the fp64 oracle.
 
-The forward picks its workgroup shape from the problem size (four query
-sub-tiles, or two sub-tiles with the keys split in two), and a third shape (one
-sub-tile, four key shares) is reachable only through ``SDPA14_FWD_SHAPE``.
-Each shape has its own merge of key shares, stage count and dropout-group
-indexing, so each is checked here on ragged sizes, both layouts, dropout,
-an additive bias and fp16.  Head dim 128 has no four-share shape; asking for
-it runs the two-by-two shape, which the test also checks.
+The forward picks its workgroup shape from the problem size: four query
+sub-tiles; two sub-tiles with the keys split in two; one sub-tile with the keys
+split in four; or (causal, head dim 64) a split launch whose last rows per head
+take 32-row, four-share workgroups with 32-key tiles and the rest two by two.
+``SDPA14_FWD_SHAPE`` (1-4) forces one.  Each shape has its own merge of key
+shares, stage count and dropout-group indexing, so each is checked here on
+ragged sizes, both layouts, dropout, an additive bias and fp16.  Head dim 128
+has no four-share shape and the split launch is causal with head dim 64;
+otherwise asking for them runs the two-by-two shape, which the test also
+checks.
 """
 
 import pytest
@@ -27,10 +30,13 @@ CASES = [
     (1, 3, 257, 129, 64, "BHSE", True, 0.0, "1hqk", torch.bfloat16),
     (2, 1, 96, 300, 64, "BSHE", False, 0.1, "qk", torch.bfloat16),
     (1, 2, 200, 264, 64, "BHSE", True, 0.1, "qk", torch.float16),
+    # Both kinds of the split launch (384 rows two by two, 316 in 32-row tiles).
+    (1, 2, 700, 700, 64, "BHSE", True, 0.1, "qk", torch.bfloat16),
+    (2, 1, 640, 640, 64, "BSHE", True, 0.0, None, torch.float16),
 ]
 
 
-@pytest.mark.parametrize("shape", [1, 2, 3])
+@pytest.mark.parametrize("shape", [1, 2, 3, 4])
 @pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,p,bias_kind,dtype", CASES)
 def test_forward_shape_parity(monkeypatch, shape, B, H, Sq, Sk, E, layout, causal, p, bias_kind,
                               dtype):
