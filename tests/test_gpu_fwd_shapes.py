@@ -33,6 +33,9 @@ CASES = [
     # Both kinds of the split launch (384 rows two by two, 316 in 32-row tiles).
     (1, 2, 700, 700, 64, "BHSE", True, 0.1, "qk", torch.bfloat16),
     (2, 1, 640, 640, 64, "BSHE", True, 0.0, None, torch.float16),
+    # Causal with Sq != Sk (top-left: row i sees keys 0..i), both directions.
+    (1, 2, 600, 300, 64, "BHSE", True, 0.1, None, torch.bfloat16),
+    (1, 2, 520, 900, 64, "BSHE", True, 0.0, "qk", torch.bfloat16),
 ]
 
 
