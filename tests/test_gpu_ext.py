@@ -286,6 +286,10 @@ def test_everything_together_fp16_sharded_device_rng_bias():
     (2, 3, 200, 330, 64, "BSHE", False, False, False),
     (1, 2, 130, 250, 128, "BHSE", False, True, True),
     (2, 2, 256, 256, 128, "BHSE", True, False, False),
+    # Causal grids that take the split forward (32-row, four-share workgroups
+    # with 32-key tiles for the last rows of each head).
+    (2, 8, 640, 640, 64, "BSHE", True, True, True),
+    (1, 12, 1024, 1024, 64, "BHSE", True, False, False),
 ])
 def test_keep_bit_cache(B, H, Sq, Sk, E, layout, causal, f16, with_bias):
     say(f"keep-bit cache B{B} H{H} Sq{Sq} Sk{Sk} E{E} {layout} causal={causal} f16={f16} bias={with_bias}")
