@@ -258,8 +258,11 @@ int hip_status(hipError_t err, const char* what) {
   return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
-// The forward workgroup shape is chosen per problem; SDPA14_FWD_SHAPE (1, 2
-// or 3) forces one, read on every call so that a process can compare them.
+// The forward workgroup shape is chosen per problem; SDPA14_FWD_SHAPE (1-4:
+// four sub-tiles, two by two, one sub-tile with four key shares, the causal
+// split launch) forces one, read on every call so that a process can compare
+// them.  A shape the problem cannot take (3 at head dim 128, 4 without causal
+// masking or at head dim 128) runs two by two.
 TileChoice tile_choice() {
   TileChoice t{0};
   if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
