@@ -317,7 +317,10 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
       const bool grow = mx > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? mx : m_run;
-        const float alpha = fast_exp2(m_run - m_new);
+        // A row that has seen only hidden keys (-inf bias entries) keeps
+        // m_run = -inf while another row of the wave grows: its sum and O are
+        // still zero, and -inf - -inf must not turn them into NaN.
+        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
@@ -405,8 +408,9 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
         const float m_o = src[(NEB * 16) * 64 + lane];
         const float l_o = src[(NEB * 16 + 1) * 64 + lane];
         const float m_new = fmaxf(m_run, m_o);
-        const float a_s = fast_exp2(m_run - m_new);
-        const float a_o = fast_exp2(m_o - m_new);
+        // A share whose keys were all hidden has m = -inf and contributes nothing.
+        const float a_s = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+        const float a_o = (m_o == -INFINITY) ? 0.f : fast_exp2(m_o - m_new);
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll

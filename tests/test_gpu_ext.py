@@ -45,7 +45,7 @@ def test_sharded_dropout_draws_the_whole_problem_mask(B, H, S, E, causal, p, cut
                                        head_offset=h0, heads_total=H)
         torch.cuda.synchronize()
         say(f"  heads {h0}:{h1}")
-        assert_out(host64(out), ref_out[sl])
+        assert_out(host64(out), ref_out[sl], dtype=out.dtype)
         assert_lse(lse.cpu().double().numpy(), ref_lse[sl])
         assert_grads([("dq", host64(dq), ref_dq[sl]), ("dk", host64(dk), ref_dk[sl]),
                       ("dv", host64(dv), ref_dv[sl])])
@@ -210,16 +210,32 @@ def test_zero_bias_equals_no_bias():
         assert (a.float() - b.float()).abs().max().item() <= 2e-2
 
 
-def test_inference_forward_without_lse():
-    say("inference forward: lse not written, out identical to the training forward")
-    q, k, v, _ = workloads.draw(2, 3, 300, 300, 64, 21, 1.0, "BHSE", device="cuda")
-    sdpa.sdpa_set_rng_state(3, 30)
-    o1, l1, s1, f1 = sdpa.sdpa_fwd_ext(q, k, v, 0.1, True, need_lse=False)
-    sdpa.sdpa_set_rng_state(3, 30)
-    o2, l2, s2, f2 = sdpa.sdpa_fwd(q, k, v, 0.1, True)
+@pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,p,with_bias", [
+    (2, 3, 300, 300, 64, "BHSE", True, 0.1, False),
+    (1, 4, 200, 333, 128, "BSHE", False, 0.0, True),
+    (2, 12, 1024, 1024, 64, "BHSE", True, 0.0, False),
+])
+def test_inference_forward_against_the_oracle(B, H, Sq, Sk, E, layout, causal, p, with_bias):
+    say(f"inference forward B{B} H{H} Sq{Sq} Sk{Sk} E{E} {layout} causal={causal} p={p} "
+        f"bias={with_bias}: no lse written, out against the oracle")
+    q, k, v, _ = workloads.draw(B, H, Sq, Sk, E, 21, 1.0, layout, device="cuda")
+    bias = None
+    if with_bias:
+        pad = (Sk + 7) // 8 * 8
+        g = torch.Generator("cpu").manual_seed(35)
+        bias = torch.randn((1, H, Sq, pad), generator=g).to(torch.bfloat16).to("cuda")[..., :Sk]
+    seed, off = 3, 30
+    sdpa.sdpa_set_rng_state(seed, off)
+    out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, p, causal, need_lse=False, bias=bias)
     torch.cuda.synchronize()
-    assert l1 is None and (s1, f1) == (s2, f2)
-    assert torch.equal(o1, o2)
+    assert lse is None and (s, o) == (seed, off)
+    ref_out, _ = sdpa_ref.fwd(q, k, v, p, causal, None, seed, off, bias=bias)
+    assert_out(host64(out), ref_out)
+    # The training forward computes the same rows the same way.
+    sdpa.sdpa_set_rng_state(seed, off)
+    out2, _, _, _ = sdpa.sdpa_fwd_ext(q, k, v, p, causal, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
 
 
 def test_minus_infinity_bias_hides_keys_like_the_causal_mask():
@@ -252,7 +268,7 @@ def test_bias_degenerate_sizes(Sq, Sk):
         torch.cuda.synchronize()
         ref_out, ref_lse = sdpa_ref.fwd(q, k, v, 0.0, causal, bias=bias)
         ref_g = sdpa_ref.bwd(do, q, k, v, 0.0, causal, bias=bias)
-        assert_out(host64(out), ref_out)
+        assert_out(host64(out), ref_out, dtype=out.dtype)
         assert_lse(lse.cpu().double().numpy(), ref_lse)
         assert_grads([(n, host64(a), r) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
 
@@ -276,7 +292,7 @@ def test_everything_together_fp16_sharded_device_rng_bias():
                               heads_total=H, rng_used=used, bias=bias[:, h0:h1])
     torch.cuda.synchronize()
     assert state.tolist() == [seed, off + philox_ref.offset_advance(B, H, S, S)]
-    assert_out(host64(out), ref_out[sl])
+    assert_out(host64(out), ref_out[sl], dtype=out.dtype)
     assert_lse(lse.cpu().double().numpy(), ref_lse[sl])
     assert_grads([(n, host64(a), r[sl]) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
 
@@ -323,3 +339,39 @@ def test_keep_bit_cache(B, H, Sq, Sk, E, layout, causal, f16, with_bias):
     if causal:
         visible = visible.tril()
     assert torch.equal(bits.to(torch.uint8)[..., visible], mask[..., visible])
+
+
+def _hidden_key_bias(kind: str, S: int) -> torch.Tensor:
+    """[S, S] bias of 0 on visible keys and -inf on hidden ones; every row keeps
+    its own key.  'window': keys i-15 .. i+15; 'blocks': 48-key diagonal blocks."""
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    if kind == "window":
+        vis = (j - i).abs() <= 15
+    else:
+        vis = (i // 48) == (j // 48)
+    b = torch.zeros(S, S).masked_fill(~vis, float("-inf"))
+    return b.to(torch.bfloat16).to("cuda")
+
+
+@pytest.mark.parametrize("shape", [1, 2, 3, 4])
+@pytest.mark.parametrize("kind", ["window", "blocks"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_whose_first_tiles_are_all_hidden(monkeypatch, shape, kind, causal):
+    # Rows of one wave reach their first visible key in different tiles, and
+    # with key shares some share of a row sees no visible key at all: the
+    # online softmax and the share merge must not turn -inf - -inf into NaN.
+    say(f"hidden-key bias {kind} causal={causal} forward shape {shape}")
+    monkeypatch.setenv("SDPA14_FWD_SHAPE", str(shape))
+    B, H, S, E = 1, 2, 304, 64
+    q, k, v, do = workloads.draw(B, H, S, S, E, 36, 1.0, "BHSE", device="cuda")
+    bias = _hidden_key_bias(kind, S)
+    out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, 0.0, causal, bias=bias)
+    grads = sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, 0.0, causal, s, o, bias=bias)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    ref_out, ref_lse = sdpa_ref.fwd(q, k, v, 0.0, causal, bias=bias)
+    ref_g = sdpa_ref.bwd(do, q, k, v, 0.0, causal, bias=bias)
+    assert_out(host64(out), ref_out)
+    assert_lse(lse.cpu().double().numpy(), ref_lse)
+    assert_grads([(n, host64(a), r) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
