@@ -29,6 +29,12 @@
  *     dropout support for mem eff", Summary: RNG state handed from forward to
  *     backward; absolute index for RNG state indexing).
  *   - E == Ev is required (nvFuser issue 2278, the SdpaFwdOp follow-up).
+ *   - non-finite inputs follow the definition in the forward: a NaN or an
+ *     infinity in query row i makes out row i and LSE row i NaN, and a NaN in
+ *     key row j makes NaN the rows that can see key j; every other row is
+ *     exactly the row of the same call without it.  A NaN in v or dout makes
+ *     NaN the outputs whose sums contain it and possibly others (a zero
+ *     probability times NaN is NaN inside a tile).
  *
  * Tensors: logical shape [B, H, S, E] with arbitrary element strides for the
  * first three dimensions and unit stride for E.  This covers both stride orders
@@ -45,7 +51,13 @@
  * Errors: every compute call returns an sdpa_status.  On a validation error
  * nothing is enqueued, outputs and the RNG state are untouched, and
  * sdpa_last_error() (per thread) describes the problem.  No C++ exception
- * crosses this boundary.
+ * crosses this boundary.  When the HIP runtime refuses a launch the call
+ * returns SDPA_ERR_HIP; a forward then takes back its RNG advance (unless
+ * another call has moved the state since), because it drew no bits.  For
+ * testing that path without a GPU, the environment variable
+ * SDPA14_FAIL_LAUNCH (set and not "0", read on every call) makes each compute
+ * call return SDPA_ERR_HIP after validation and before any HIP call: nothing
+ * is enqueued and the RNG state is untouched.
  */
 #ifndef SDPA14_H
 #define SDPA14_H

@@ -127,8 +127,21 @@ def _check(rc: int) -> None:
     raise SdpaError(msg)
 
 
-def describe(t: torch.Tensor) -> SdpaTensor:
-    """C descriptor of a 4-D tensor (logical [B, H, S, E], strides in elements)."""
+def _on_device(t: torch.Tensor, device: torch.device | None, name: str) -> None:
+    """The C side cannot tell host from device pointers: check here, before any call."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a tensor on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the device of q)")
+
+
+def describe(t: torch.Tensor, device: torch.device | None = None,
+             name: str = "tensor") -> SdpaTensor:
+    """C descriptor of a 4-D device tensor (logical [B, H, S, E], strides in elements).
+
+    ``device``, when given, is the device every tensor of the call must be on.
+    """
+    _on_device(t, device, name)
     if t.dim() != 4:
         raise ValueError(f"expected a 4-D [B, H, S, E] tensor, got shape {tuple(t.shape)}")
     d = SdpaTensor()
@@ -138,6 +151,19 @@ def describe(t: torch.Tensor) -> SdpaTensor:
         d.size[i] = t.shape[i]
         d.stride[i] = t.stride(i)
     return d
+
+
+def _check_lse(lse, q: torch.Tensor) -> None:
+    """lse: contiguous float32 [B, H, Sq] on q's device."""
+    _on_device(lse, q.device, "lse")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+
+
+def _check_workspace(ws, q: torch.Tensor) -> None:
+    _on_device(ws, q.device, "workspace")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
 
 
 def _stream(device: torch.device) -> int:
@@ -157,13 +183,14 @@ def sdpa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dropout_p: float
     to a contiguous fp32 ``[B, H, Sq]`` tensor.
     """
     lib = load_library()
+    _on_device(q, None, "q")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
-        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
-    dq_, dk_, dv_, do_ = describe(q), describe(k), describe(v), describe(out)
+    _check_lse(lse, q)
+    dev = q.device
+    dq_, dk_, dv_, do_ = (describe(t, dev, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
     seed, offset = ctypes.c_uint64(), ctypes.c_uint64()
     with torch.cuda.device(q.device):
         rc = lib.sdpa_fwd(ctypes.byref(dq_), ctypes.byref(dk_), ctypes.byref(dv_),
@@ -187,14 +214,18 @@ def sdpa_bwd(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: i
     ``sdpa_bwd_workspace_size(B, H, Sq)`` bytes; one is allocated when omitted.
     """
     lib = load_library()
+    _on_device(q, None, "q")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     B, H, Sq = q.shape[0], q.shape[1], q.shape[2]
+    _check_lse(lse, q)
     if workspace is None:
         workspace = torch.empty(max(lib.sdpa_bwd_workspace_size(B, H, Sq), 256),
                                 dtype=torch.uint8, device=q.device)
-    descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
+    _check_workspace(workspace, q)
+    descs = [describe(t, q.device, n) for t, n in zip(
+        (dout, q, k, v, out, dq, dk, dv), ("dout", "q", "k", "v", "out", "dq", "dk", "dv"))]
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                           float(dropout_p), int(bool(is_causal)), int(seed), int(offset),
@@ -205,11 +236,11 @@ def sdpa_bwd(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: i
     return dq, dk, dv
 
 
-def _rng_buffer(t, name: str):
+def _rng_buffer(t, name: str, device=None):
     if t is None:
         return None
-    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype in (torch.int64, torch.uint64)
-            and t.numel() == 2 and t.is_contiguous()):
+    _on_device(t, device, name)
+    if not (t.dtype in (torch.int64, torch.uint64) and t.numel() == 2 and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous device int64 tensor of 2 elements "
                          "(seed, offset)")
     return t.data_ptr()
@@ -220,24 +251,25 @@ def sdpa_keep_bits_size(B: int, H: int, Sq: int, Sk: int) -> int:
     return int(load_library().sdpa_keep_bits_size(int(B), int(H), int(Sq), int(Sk)))
 
 
-def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None, keep_bits=None):
+def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None, keep_bits=None,
+         device=None):
     """The options block and the objects it points into (keep both alive for the call)."""
     e = SdpaExt()
     if keep_bits is not None:
-        if not (isinstance(keep_bits, torch.Tensor) and keep_bits.is_cuda
-                and keep_bits.is_contiguous()):
+        _on_device(keep_bits, device, "keep_bits")
+        if not keep_bits.is_contiguous():
             raise ValueError("keep_bits must be a contiguous device tensor")
         e.keep_bits = keep_bits.data_ptr()
     e.head_offset = int(head_offset)
     e.heads_total = int(heads_total)
-    e.rng_state = _rng_buffer(rng_state, "rng_state")
-    e.rng_used = _rng_buffer(rng_used, "rng_used")
+    e.rng_state = _rng_buffer(rng_state, "rng_state", device)
+    e.rng_used = _rng_buffer(rng_used, "rng_used", device)
     keep = None
     if bias is not None:
         if bias.dim() > 4:
             raise ValueError("bias must broadcast to [B, H, Sq, Sk]")
         full = bias.expand(*shape)  # broadcast dimensions get stride 0
-        desc = describe(full)
+        desc = describe(full, device, "bias")
         e.bias = ctypes.pointer(desc)
         keep = (full, desc)
     return e, keep
@@ -260,18 +292,19 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
     ``sdpa_keep_bits_size`` bytes) receives the dropout keep bits for a backward.
     """
     lib = load_library()
+    _on_device(q, None, "q")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and need_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    if need_lse and (lse.dtype != torch.float32 or not lse.is_contiguous()
-                     or tuple(lse.shape) != tuple(q.shape[:3])):
-        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
-    if not need_lse:
+    if need_lse:
+        _check_lse(lse, q)
+    else:
         lse = None
-    dq_, dk_, dv_, do_ = describe(q), describe(k), describe(v), describe(out)
+    dev = q.device
+    dq_, dk_, dv_, do_ = (describe(t, dev, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
     ext, _keep = _ext(head_offset, heads_total, rng_state, rng_used, bias,
-                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits)
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, dev)
     seed, offset = ctypes.c_uint64(), ctypes.c_uint64()
     with torch.cuda.device(q.device):
         rc = lib.sdpa_fwd_ext(ctypes.byref(dq_), ctypes.byref(dk_), ctypes.byref(dv_),
@@ -295,16 +328,20 @@ def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, see
     and ``seed`` / ``offset`` are ignored.
     """
     lib = load_library()
+    _on_device(q, None, "q")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     B, H, Sq = q.shape[0], q.shape[1], q.shape[2]
+    _check_lse(lse, q)
     if workspace is None:
         workspace = torch.empty(max(lib.sdpa_bwd_workspace_size(B, H, Sq), 256),
                                 dtype=torch.uint8, device=q.device)
-    descs = [describe(t) for t in (dout, q, k, v, out, dq, dk, dv)]
+    _check_workspace(workspace, q)
+    descs = [describe(t, q.device, n) for t, n in zip(
+        (dout, q, k, v, out, dq, dk, dv), ("dout", "q", "k", "v", "out", "dq", "dk", "dv"))]
     ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
-                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits)
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device)
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd_ext(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                               float(dropout_p), int(bool(is_causal)), int(seed), int(offset),

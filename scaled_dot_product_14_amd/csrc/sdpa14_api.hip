@@ -258,6 +258,17 @@ int hip_status(hipError_t err, const char* what) {
   return fail(SDPA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
+// SDPA14_FAIL_LAUNCH (set and not "0") makes every compute call fail as if
+// the HIP runtime had refused its launch: the call returns SDPA_ERR_HIP
+// before any HIP call, so error propagation can be tested without a GPU and
+// without faulting one.  Read on every call.
+bool forced_launch_failure(const char* what) {
+  const char* s = getenv("SDPA14_FAIL_LAUNCH");
+  if (s == nullptr || s[0] == '\0' || (s[0] == '0' && s[1] == '\0')) return false;
+  fail(SDPA_ERR_HIP, "%s: launch failure forced by SDPA14_FAIL_LAUNCH; nothing was enqueued", what);
+  return true;
+}
+
 // The forward workgroup shape is chosen per problem; SDPA14_FWD_SHAPE (1-4:
 // four sub-tiles, two by two, one sub-tile with four key shares, the causal
 // split launch) forces one, read on every call so that a process can compare
@@ -306,6 +317,7 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   const bool drop = dropout_p > 0.0;
   const uint64_t advance = offset_advance(dq.B, e.heads_total, dq.S, dk.S);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (forced_launch_failure("forward launch")) return SDPA_ERR_HIP;
 
   uint64_t s0 = 0, o0 = 0;
   if (e.rng_state == nullptr) {
@@ -314,6 +326,13 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
     o0 = g_rng_offset;
     if (drop) g_rng_offset += advance;
   }
+  // A forward whose launch failed drew no bits: its advance is taken back
+  // unless another call has moved the state since.
+  auto undo_advance = [&] {
+    if (!drop || e.rng_state != nullptr) return;
+    std::lock_guard<std::mutex> lk(g_rng_mu);
+    if (g_rng_seed == s0 && g_rng_offset == o0 + advance) g_rng_offset = o0;
+  };
   if (e.rng_state == nullptr && seed) *seed = s0;
   if (e.rng_state == nullptr && offset) *offset = o0;
   (void)hipGetLastError();
@@ -346,6 +365,7 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
     return launch_fwd(p, (int)dq.E, is_causal != 0, drop, dq.dtype == SDPA_F16, tile_choice(),
                       st);
   });
+  if (err != hipSuccess) undo_advance();
   return hip_status(err, "forward launch");
 }
 
@@ -432,6 +452,7 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   const int E = (int)dqi.E;
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (forced_launch_failure("backward launch")) return SDPA_ERR_HIP;
   (void)hipGetLastError();
   const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
                                       [&] {
@@ -494,6 +515,7 @@ int sdpa_debug_dropout_mask(uint64_t seed, uint64_t offset, double dropout_p, in
   p.Sq = (int)Sq;
   p.Sk = (int)Sk;
   p.drop = make_dropout(dropout_p, seed, offset, H, 0, nullptr);
+  if (forced_launch_failure("mask launch")) return SDPA_ERR_HIP;
   (void)hipGetLastError();
   return hip_status(launch_mask(p, reinterpret_cast<hipStream_t>(stream)), "mask launch");
 }

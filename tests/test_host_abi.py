@@ -272,3 +272,103 @@ def test_keep_bits_alignment_checked(lib):
                           ctypes.byref(ext), None)
     assert rc == bnd.SDPA_ERR_UNSUPPORTED and "keep_bits" in _err(lib)
     assert bnd.sdpa_get_rng_state() == (61, 62)
+
+
+# ---- launch failures (SDPA_ERR_HIP) ------------------------------------------------
+
+
+def test_forced_launch_failure_forward(lib, monkeypatch):
+    # Valid arguments; the hook stands in for a launch the runtime refuses.  The
+    # call must fail before any HIP call (there is no GPU here), leave the RNG
+    # state as it was and say why.
+    monkeypatch.setenv("SDPA14_FAIL_LAUNCH", "1")
+    bnd.sdpa_set_rng_state(71, 72)
+    rc = _fwd(lib, p=0.1)
+    assert rc == bnd.SDPA_ERR_HIP, (rc, _err(lib))
+    assert "SDPA14_FAIL_LAUNCH" in _err(lib) and "forward" in _err(lib)
+    assert bnd.sdpa_get_rng_state() == (71, 72)
+    with pytest.raises(bnd.SdpaError, match="SDPA_ERR_HIP: forward launch"):
+        bnd._check(rc)
+
+
+def test_forced_launch_failure_backward_and_mask(lib, monkeypatch):
+    monkeypatch.setenv("SDPA14_FAIL_LAUNCH", "yes")
+    bnd.sdpa_set_rng_state(73, 74)
+    rc = _bwd(lib, p=0.1)
+    assert rc == bnd.SDPA_ERR_HIP and "backward" in _err(lib)
+    with pytest.raises(bnd.SdpaError, match="backward launch"):
+        bnd._check(rc)
+    rc = lib.sdpa_debug_dropout_mask(1, 2, 0.1, 1, 1, 4, 4, FAKE, None)
+    assert rc == bnd.SDPA_ERR_HIP and "mask" in _err(lib)
+    assert bnd.sdpa_get_rng_state() == (73, 74)
+
+
+def test_forced_launch_failure_comes_after_validation(lib, monkeypatch):
+    # An invalid call still reports its own error, not the launch failure.
+    monkeypatch.setenv("SDPA14_FAIL_LAUNCH", "1")
+    rc = _fwd(lib, p=1.0)
+    assert rc == bnd.SDPA_ERR_INVALID and "dropout" in _err(lib)
+
+
+def test_launch_failure_hook_off_when_zero(lib, monkeypatch):
+    # "0" disables the hook; the call then fails only on its bad argument.
+    monkeypatch.setenv("SDPA14_FAIL_LAUNCH", "0")
+    rc = _fwd(lib, p=-1.0)
+    assert rc == bnd.SDPA_ERR_INVALID
+
+
+@pytest.mark.parametrize("rc,exc", [
+    (bnd.SDPA_ERR_INVALID, ValueError),
+    (bnd.SDPA_ERR_WORKSPACE, ValueError),
+    (bnd.SDPA_ERR_UNSUPPORTED, NotImplementedError),
+    (bnd.SDPA_ERR_HIP, bnd.SdpaError),
+])
+def test_status_maps_to_python_exception(lib, rc, exc):
+    with pytest.raises(exc):
+        bnd._check(rc)
+
+
+# ---- the Python binding checks devices before calling the library ----------------
+
+
+class _NoLibrary:
+    """Stands in for the loaded library: any use of it fails the test."""
+
+    def __getattr__(self, name):
+        raise AssertionError(f"library function {name} was reached")
+
+
+@pytest.fixture
+def no_library(monkeypatch):
+    monkeypatch.setattr(bnd, "_lib", _NoLibrary())
+
+
+def _host_inputs(S=64, E=64):
+    import torch
+
+    g = torch.Generator("cpu").manual_seed(0)
+    return [torch.randn((1, 2, S, E), generator=g).to(torch.bfloat16) for _ in range(4)]
+
+
+def test_host_tensors_rejected_before_the_library(no_library):
+    import torch
+
+    q, k, v, do = _host_inputs()
+    with pytest.raises(ValueError, match="GPU"):
+        sdpa.sdpa_fwd(q, k, v, 0.0, True)
+    with pytest.raises(ValueError, match="GPU"):
+        sdpa.sdpa_fwd_ext(q, k, v, 0.0, True, need_lse=False)
+    lse = torch.zeros((1, 2, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        sdpa.sdpa_bwd(do, q, k, v, q, lse, 0.0, True, 0, 0)
+    with pytest.raises(ValueError, match="GPU"):
+        sdpa.sdpa_bwd_ext(do, q, k, v, q, lse, 0.0, True)
+
+
+def test_describe_rejects_host_and_meta_tensors():
+    import torch
+
+    with pytest.raises(ValueError, match="GPU"):
+        bnd.describe(torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        bnd.describe(torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="meta"))
