@@ -30,9 +30,10 @@
  *     backward; absolute index for RNG state indexing).
  *   - E == Ev is required (nvFuser issue 2278, the SdpaFwdOp follow-up).
  *   - non-finite inputs follow the definition in the forward: a NaN or an
- *     infinity in query row i makes out row i and LSE row i NaN, and a NaN in
- *     key row j makes NaN the rows that can see key j; every other row is
- *     exactly the row of the same call without it.  A NaN in v or dout makes
+ *     infinity in query row i makes out row i NaN and LSE row i non-finite
+ *     (NaN, or -inf when every score of the row is -inf), and a NaN in key
+ *     row j makes NaN the out and LSE rows that can see key j; every other row
+ *     is exactly the row of the same call without it.  A NaN in v or dout makes
  *     NaN the outputs whose sums contain it and possibly others (a zero
  *     probability times NaN is NaN inside a tile).
  *

@@ -1,10 +1,17 @@
 """Shared helpers for the GPU parity tests: device transfer and error metrics.
 
 Tolerances (the targets of the method's parity statement):
-  out   max |gpu - oracle| <= 1e-2, plus the rounding of the bf16 output: an
-        element also passes when its error is within 1e-2 + half a bf16 ulp of
-        the oracle value (a bf16 number cannot be closer than half an ulp to an
-        arbitrary real; for |O| >= 4 that is already 2^-6 > 1e-2)
+  out   |gpu - oracle| <= 1e-2 on every element, compared with the unrounded
+        fp64 oracle.  The one exemption is an element the output format itself
+        cannot bring within 1e-2: its rounding floor |round(ref) - ref| (round
+        to nearest in the output's own format, bf16 or fp16) plus the kernel's
+        pre-rounding budget 2^-8 |ref| (probabilities enter the P.V product as
+        16-bit values) exceeds 1e-2.  Such an element must then be one of the
+        two representable neighbours of ref.  For bf16 this only happens at
+        |ref| >= 2 (half an ulp is 2^-6 > 1e-2 from |ref| = 4 on); for fp16
+        never below |ref| = 2.56, where an ulp is already below 1e-2.  Every
+        check prints the strict maximum, the largest floor and the number of
+        exempt elements.
   lse   max |gpu - oracle| <= 1e-3
   grads ||g - g_ref||_F / max(||g_ref||_F, 1e-3 * sqrt(n)) <= 2e-2 per tensor; the
         floor (an RMS of 1e-3) only matters where the exact gradient vanishes,
@@ -13,6 +20,7 @@ Tolerances (the targets of the method's parity statement):
 """
 
 import math
+import os
 import sys
 
 import numpy as np
@@ -42,18 +50,40 @@ def host64(t) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
 
-def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
-    """Half the bf16 spacing at |x| (8 significant bits)."""
+def neighbours(x: np.ndarray, dtype=torch.bfloat16):
+    """The two values of the 16-bit format bracketing each float64 x (equal when
+    x is representable), computed exactly in float64."""
+    mant, emin = (8, -126) if dtype == torch.bfloat16 else (11, -14)
     ax = np.abs(x)
     e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    return np.where(ax > 0, np.exp2(e - 8), 0.0)
+    ulp = np.exp2(np.maximum(e, emin) - (mant - 1))
+    lo = np.floor(x / ulp) * ulp
+    hi = np.where(lo == x, lo, lo + ulp)
+    return lo, hi
 
 
-def out_errors(gpu: np.ndarray, ref: np.ndarray):
-    """(strict max abs error, number of elements failing the bf16-aware bar)."""
+def out_report(gpu: np.ndarray, ref: np.ndarray, dtype=torch.bfloat16) -> dict:
+    """Strict and exempt error figures of one output comparison (see the module note)."""
     err = np.abs(gpu - ref)
-    bad = err > OUT_TOL + bf16_half_ulp(ref)
-    return float(err.max()), int(bad.sum())
+    lo, hi = neighbours(ref, dtype)
+    floor = np.minimum(ref - lo, hi - ref)
+    over = err > OUT_TOL
+    eligible = floor + np.ldexp(np.abs(ref), -8) > OUT_TOL
+    neighbour = (gpu == lo) | (gpu == hi)
+    exempt = over & eligible & neighbour
+    return {
+        "strict_max": float(err.max()) if err.size else 0.0,
+        "floor_max": float(floor.max()) if floor.size else 0.0,
+        "n_floor_over": int((floor > OUT_TOL).sum()),
+        "n_over": int(over.sum()),
+        "n_exempt": int(exempt.sum()),
+        "n_fail": int((over & ~exempt).sum()),
+        "n": int(err.size),
+        "dtype": str(dtype).split(".")[-1],
+    }
+
+
+REPORT = []  # every out comparison of the session, for the parity report
 
 
 def rel_fro(gpu: np.ndarray, ref: np.ndarray) -> float:
@@ -61,10 +91,14 @@ def rel_fro(gpu: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm((gpu - ref).ravel()) / max(np.linalg.norm(ref.ravel()), floor))
 
 
-def assert_out(gpu, ref, what="out"):
-    strict, nbad = out_errors(gpu, ref)
-    say(f"  {what}: max abs err {strict:.3e} (bf16-aware failures: {nbad})")
-    assert nbad == 0, f"{what}: {nbad} elements beyond 1e-2 + half bf16 ulp (max {strict})"
+def assert_out(gpu, ref, what="out", dtype=torch.bfloat16):
+    r = out_report(gpu, ref, dtype)
+    r["what"] = what
+    r["test"] = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    REPORT.append(r)
+    say(f"  {what}: max abs err {r['strict_max']:.3e}, rounding floor max {r['floor_max']:.3e}, "
+        f"exempt {r['n_exempt']} of {r['n']} ({r['dtype']})")
+    assert r["n_fail"] == 0, f"{what}: {r['n_fail']} elements beyond 1e-2 and not exempt ({r})"
 
 
 def assert_lse(gpu, ref):

@@ -15,3 +15,19 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def root_dir():
     return ROOT
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With SDPA14_PARITY_REPORT set, write every output comparison of the
+    session (strict maximum, rounding floor, exempt count) as JSON lines."""
+    path = os.environ.get("SDPA14_PARITY_REPORT")
+    if not path:
+        return
+    import json
+
+    from tests import _util
+
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        for r in _util.REPORT:
+            f.write(json.dumps(r) + "\n")

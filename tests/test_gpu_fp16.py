@@ -43,6 +43,6 @@ def test_fp16_parity(B, H, Sq, Sk, E, layout, causal, p, with_bias):
     assert out.dtype == torch.float16 and dq.dtype == torch.float16
     ref_out, ref_lse = sdpa_ref.fwd(q, k, v, p, causal, None, seed, off, bias=bias)
     ref_dq, ref_dk, ref_dv = sdpa_ref.bwd(do, q, k, v, p, causal, seed, off, None, bias=bias)
-    assert_out(host64(out), ref_out)
+    assert_out(host64(out), ref_out, dtype=out.dtype)
     assert_lse(lse.cpu().double().numpy(), ref_lse)
     assert_grads([("dq", host64(dq), ref_dq), ("dk", host64(dk), ref_dk), ("dv", host64(dv), ref_dv)])

@@ -62,5 +62,5 @@ def test_forward_shape_parity(monkeypatch, shape, B, H, Sq, Sk, E, layout, causa
     torch.cuda.synchronize()
     assert (s, o) == (seed, off)
     ref_out, ref_lse = sdpa_ref.fwd(q, k, v, p, causal, None, seed, off, bias=bias)
-    assert_out(host64(out), ref_out)
+    assert_out(host64(out), ref_out, dtype=out.dtype)
     assert_lse(lse.cpu().double().numpy(), ref_lse)

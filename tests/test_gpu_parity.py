@@ -58,25 +58,50 @@ def test_named_workload(name):
         assert sdpa.sdpa_get_rng_state() == (w.rng_seed, w.rng_offset + adv)
 
 
-def test_long_cross_attention_sampled_heads():
+def xcd_group_heads(B, H):
+    """One (b, h) from every group of heads the kernels place on one XCD.
+
+    Both kernels deal a head's workgroups to one of the 8 XCDs; with B*H a
+    multiple of 8, XCD x holds heads x*B*H/8 .. (x+1)*B*H/8 - 1 (flattened
+    b*H + h).  The pick moves through the positions inside the groups."""
+    n = B * H
+    per = n // 8
+    flat = [x * per + (x % per) for x in range(8)]
+    return [(f // H, f % H) for f in flat]
+
+
+def test_long_cross_attention_every_xcd_group():
     w = workloads.WORKLOADS["b1_h32_q4096_k8192_d128_cross"]
     q, k, v, do = workloads.make_inputs(w, device="cuda")
-    say("case long cross: full GPU run, oracle on sampled rows and heads")
+    say("case long cross: full GPU run; oracle on 8 whole heads (one per XCD group) "
+        "and on rows of every 128-row query tile of the other heads")
     out, lse, seed, offset, dq, dk, dv = run_gpu(q, k, v, do, 0.0, False)
-    # Forward: 128 sampled rows in each of 6 heads.
-    rng = np.random.default_rng(5)
     qc, kc, vc, doc = (t.cpu() for t in (q, k, v, do))
     o_h, l_h = host64(out), lse.cpu().double().numpy()
-    for b, h in heads_subset(w.B, w.H, 6, seed=1):
-        rows = np.sort(rng.choice(w.Sq, size=128, replace=False))
-        ro, rl = sdpa_ref.fwd_rows(qc, kc, vc, b, h, rows, 0.0, False)
-        assert_out(o_h[b, h, rows], ro, what=f"out head {h}")
-        assert_lse(l_h[b, h, rows], rl)
-    # Backward: two whole heads.
-    heads = heads_subset(w.B, w.H, 2, seed=2)
-    r_dq, r_dk, r_dv = sdpa_ref.bwd(doc, qc, kc, vc, 0.0, False, heads=heads)
+    whole = xcd_group_heads(w.B, w.H)
+    assert len({(b * w.H + h) // (w.B * w.H // 8) for b, h in whole}) == 8
+    # Forward, whole heads.
+    ref_out, ref_lse = sdpa_ref.fwd(qc, kc, vc, 0.0, False, heads=whole)
+    for b, h in whole:
+        say(f"  head {h} (whole)")
+        assert_out(o_h[b, h], ref_out[b, h], what=f"out head {h}")
+        assert_lse(l_h[b, h], ref_lse[b, h])
+    # Forward, the other heads: two rows of every 128-row query tile.
+    rng = np.random.default_rng(5)
+    for b in range(w.B):
+        for h in range(w.H):
+            if (b, h) in whole:
+                continue
+            rows = np.sort(np.concatenate([t * 128 + rng.choice(128, size=2, replace=False)
+                                           for t in range(w.Sq // 128)]))
+            ro, rl = sdpa_ref.fwd_rows(qc, kc, vc, b, h, rows, 0.0, False)
+            assert_out(o_h[b, h, rows], ro, what=f"out head {h} rows")
+            assert_lse(l_h[b, h, rows], rl)
+    # Backward: the same whole heads.
+    r_dq, r_dk, r_dv = sdpa_ref.bwd(doc, qc, kc, vc, 0.0, False, heads=whole)
     gdq, gdk, gdv = host64(dq), host64(dk), host64(dv)
-    for b, h in heads:
+    for b, h in whole:
+        say(f"  head {h} gradients")
         assert_grads([("dq", gdq[b, h], r_dq[b, h]), ("dk", gdk[b, h], r_dk[b, h]),
                       ("dv", gdv[b, h], r_dv[b, h])])
 

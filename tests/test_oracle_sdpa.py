@@ -293,3 +293,60 @@ def test_bias_finite_differences_with_dropout():
         g = grads[i]
         err = np.linalg.norm(fd - g) / max(np.linalg.norm(g), 1e-30)
         assert err <= 1e-6 or np.abs(fd - g).max() < 1e-8, (i, err)
+
+
+# ---- non-finite inputs --------------------------------------------------------
+# The definition fixes what a NaN or an infinity does: only the outputs whose
+# defining sums contain it are NaN.  A query row enters only its own row of S;
+# a key row enters column j of S, which a causal row i < j never reads.
+
+
+@pytest.mark.parametrize("bad", [math.nan, math.inf, -math.inf])
+def test_non_finite_query_row_poisons_only_its_row(bad):
+    q, k, v, _ = workloads.draw(1, 2, 40, 40, 8, 37, 1.0, "BHSE")
+    o_ref, l_ref = sdpa_ref.fwd(q, k, v, 0.0, True)
+    q2 = q.clone()
+    q2[0, 1, 17, 3] = bad
+    o, l = sdpa_ref.fwd(q2, k, v, 0.0, True)
+    assert np.isnan(o[0, 1, 17]).all() and not np.isfinite(l[0, 1, 17])
+    keep = np.ones(40, dtype=bool)
+    keep[17] = False
+    assert np.array_equal(o[0, 1, keep], o_ref[0, 1, keep])
+    assert np.array_equal(l[0, 1, keep], l_ref[0, 1, keep])
+    assert np.array_equal(o[0, 0], o_ref[0, 0]) and np.array_equal(l[0, 0], l_ref[0, 0])
+
+
+def test_nan_key_row_poisons_the_rows_that_see_it():
+    q, k, v, _ = workloads.draw(1, 1, 40, 40, 8, 38, 1.0, "BHSE")
+    o_ref, l_ref = sdpa_ref.fwd(q, k, v, 0.0, True)
+    k2 = k.clone()
+    k2[0, 0, 25, 0] = math.nan
+    o, l = sdpa_ref.fwd(q, k2, v, 0.0, True)
+    assert np.isnan(o[0, 0, 25:]).all() and np.isnan(l[0, 0, 25:]).all()
+    assert np.array_equal(o[0, 0, :25], o_ref[0, 0, :25])
+    assert np.array_equal(l[0, 0, :25], l_ref[0, 0, :25])
+
+
+def test_out_rounding_floor_file_matches_the_oracle():
+    # tests/golden/out_rounding_floor.txt is written by make_out_rounding_floor.py
+    # from the oracle alone; re-derive the small workloads' lines here.
+    import os
+
+    from tests.golden import make_out_rounding_floor as mk
+
+    rows = {}
+    with open(mk.OUT) as f:
+        for line in f:
+            if not line.startswith("#"):
+                name, *vals = line.split()
+                rows[name] = vals
+    assert set(rows) == set(workloads.WORKLOADS)
+    for name in ("tiny_causal", "tiny_bshe_wide_scores"):
+        fmax, n_floor, n_elig, amax = mk.floor_stats(workloads.WORKLOADS[name])
+        n, a, f, nf, ne = rows[name]
+        assert float(a) == pytest.approx(amax, rel=1e-6)
+        assert float(f) == pytest.approx(fmax, rel=1e-6)
+        assert (int(nf), int(ne)) == (n_floor, n_elig)
+    # No named workload has an element that a bf16 output cannot bring within 1e-2.
+    assert all(int(v[3]) == 0 for v in rows.values())
+    assert os.path.basename(mk.OUT) == "out_rounding_floor.txt"
