@@ -203,6 +203,29 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
                  void* workspace, size_t workspace_bytes, const sdpa_ext* ext,
                  sdpa_stream_t stream);
 
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The same computation as sdpa_bwd_ext, with the row pass's
+ * workspace taken from a fixed scratch array inside the library instead of
+ * from the caller: 4 MiB per device, which holds B*H*Sq <= 524288 query rows
+ * (sdpa_bwd_noalloc_max_rows()).  Larger problems are rejected with
+ * SDPA_ERR_UNSUPPORTED before anything is enqueued.  The call allocates
+ * nothing and needs no initialisation: the first call on a device looks up
+ * that device's scratch address once.  The caller passes every input and
+ * output.  All calls on one device share its scratch and each call
+ * overwrites it (nothing in it needs clearing: the row pass writes every row
+ * the main kernel reads), so calls whose work overlaps on one device (several
+ * streams, several threads) race; serialise them on one stream.
+ */
+int sdpa_bwd_noalloc(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+                     const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
+                     double dropout_p, int is_causal, uint64_t seed, uint64_t offset,
+                     double scale, const sdpa_tensor* dq, const sdpa_tensor* dk,
+                     const sdpa_tensor* dv, const sdpa_ext* ext, sdpa_stream_t stream);
+/* Largest B*H*Sq sdpa_bwd_noalloc accepts. */
+size_t sdpa_bwd_noalloc_max_rows(void);
+
 /* Bytes of the keep-bit cache (sdpa_ext.keep_bits) for a problem; 0 when a size
  * is not positive. */
 size_t sdpa_keep_bits_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk);

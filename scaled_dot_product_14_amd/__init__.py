@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     load_library,
     sdpa_bwd,
     sdpa_bwd_ext,
+    sdpa_bwd_noalloc,
+    sdpa_bwd_noalloc_max_rows,
     sdpa_bwd_workspace_size,
     sdpa_debug_dropout_mask,
     sdpa_fwd,

@@ -33,6 +33,7 @@ EXPORTED = (
     "sdpa_set_rng_state",
     "sdpa_get_rng_state", "sdpa_status_string", "sdpa_last_error",
     "sdpa_debug_dropout_mask", "sdpa_profile_enable", "sdpa_profile_read",
+    "sdpa_bwd_noalloc", "sdpa_bwd_noalloc_max_rows",
 )
 
 
@@ -90,6 +91,12 @@ def load_library(path: str = LIB_PATH):
                                  ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, P, P, P,
                                  ctypes.c_void_p, ctypes.c_size_t, E, ctypes.c_void_p]
     lib.sdpa_bwd_ext.restype = ctypes.c_int
+    lib.sdpa_bwd_noalloc.argtypes = [P, P, P, P, P, ctypes.c_void_p, ctypes.c_double,
+                                     ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                     ctypes.c_double, P, P, P, E, ctypes.c_void_p]
+    lib.sdpa_bwd_noalloc.restype = ctypes.c_int
+    lib.sdpa_bwd_noalloc_max_rows.argtypes = []
+    lib.sdpa_bwd_noalloc_max_rows.restype = ctypes.c_size_t
     lib.sdpa_keep_bits_size.argtypes = [ctypes.c_int64] * 4
     lib.sdpa_keep_bits_size.restype = ctypes.c_size_t
     lib.sdpa_bwd_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
@@ -383,3 +390,30 @@ def sdpa_profile_read(kind: int):
     ms, n = ctypes.c_double(), ctypes.c_int64()
     _check(load_library().sdpa_profile_read(int(kind), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def sdpa_bwd_noalloc_max_rows() -> int:
+    """Largest B*H*Sq the allocation-free backward accepts."""
+    return int(load_library().sdpa_bwd_noalloc_max_rows())
+
+
+def sdpa_bwd_noalloc(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int,
+                     offset: int, scale, dq, dk, dv, *, head_offset: int = 0,
+                     heads_total: int = 0, rng_used=None, bias=None, keep_bits=None):
+    """Backward that allocates nothing: the caller passes dq, dk, dv and the
+    library uses its own device-resident scratch for the row pass.  Returns
+    ``(dq, dk, dv)``.  Calls that overlap on one device race (shared scratch)."""
+    lib = load_library()
+    _on_device(q, None, "q")
+    _check_lse(lse, q)
+    descs = [describe(t, q.device, n) for t, n in zip(
+        (dout, q, k, v, out, dq, dk, dv), ("dout", "q", "k", "v", "out", "dq", "dk", "dv"))]
+    ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device)
+    with torch.cuda.device(q.device):
+        rc = lib.sdpa_bwd_noalloc(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
+                                  float(dropout_p), int(bool(is_causal)), int(seed), int(offset),
+                                  _scale_arg(scale), *(ctypes.byref(d) for d in descs[5:]),
+                                  ctypes.byref(ext), _stream(q.device))
+    _check(rc)
+    return dq, dk, dv

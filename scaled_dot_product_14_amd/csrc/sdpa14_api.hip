@@ -280,6 +280,48 @@ TileChoice tile_choice() {
   return t;
 }
 
+// ---- scratch of the allocation-free backward --------------------------------
+// The row pass's two fp32 planes (-D and the base-2 LSE of every query row),
+// 8 bytes per row, live in this array for sdpa_bwd_noalloc.  Each device holds
+// its own copy until the process ends.  Host code never passes the array's
+// name to a kernel: on the host it is only a stand-in for the symbol, and the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = size_t(4) << 20;  // 524288 query rows
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (looked up on the first call per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_status(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SDPA_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_status(err, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+      return fail(SDPA_ERR_HIP, "scratch symbol has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SDPA_OK;
+}
+
+int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+             const sdpa_tensor* v, const sdpa_tensor* out, const float* lse, double dropout_p,
+             int is_causal, uint64_t seed, uint64_t offset, double scale, const sdpa_tensor* dq,
+             const sdpa_tensor* dk, const sdpa_tensor* dv, void* workspace,
+             size_t workspace_bytes, bool use_scratch, const sdpa_ext* ext,
+             sdpa_stream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +426,33 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
                  const sdpa_tensor* dq, const sdpa_tensor* dk, const sdpa_tensor* dv,
                  void* workspace, size_t workspace_bytes, const sdpa_ext* ext,
                  sdpa_stream_t stream) {
+  return bwd_call(dout, q, k, v, out, lse, dropout_p, is_causal, seed, offset, scale, dq, dk, dv,
+                  workspace, workspace_bytes, false, ext, stream);
+}
+
+int sdpa_bwd_noalloc(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+                     const sdpa_tensor* v, const sdpa_tensor* out, const float* lse,
+                     double dropout_p, int is_causal, uint64_t seed, uint64_t offset,
+                     double scale, const sdpa_tensor* dq, const sdpa_tensor* dk,
+                     const sdpa_tensor* dv, const sdpa_ext* ext, sdpa_stream_t stream) {
+  return bwd_call(dout, q, k, v, out, lse, dropout_p, is_causal, seed, offset, scale, dq, dk, dv,
+                  nullptr, 0, true, ext, stream);
+}
+
+size_t sdpa_bwd_noalloc_max_rows(void) { return kScratchBytes / 8u; }
+
+}  // extern "C"
+
+namespace {
+
+// The backward of sdpa_bwd_ext (workspace given by the caller) and of
+// sdpa_bwd_noalloc (use_scratch: the library's device-resident scratch).
+int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k,
+             const sdpa_tensor* v, const sdpa_tensor* out, const float* lse, double dropout_p,
+             int is_causal, uint64_t seed, uint64_t offset, double scale, const sdpa_tensor* dq,
+             const sdpa_tensor* dk, const sdpa_tensor* dv, void* workspace,
+             size_t workspace_bytes, bool use_scratch, const sdpa_ext* ext,
+             sdpa_stream_t stream) {
   Desc ddo, dqi, dki, dvi, dout_i, dqo, dko, dvo;
   int rc;
   if ((rc = check_tensor(dout, "dout", &ddo))) return rc;
@@ -408,11 +477,19 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   if ((rc = check_dropout(dropout_p))) return rc;
   float sc;
   if ((rc = resolve_scale(scale, dqi.E, &sc))) return rc;
-  if (workspace == nullptr) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < bwd_workspace_bytes(dqi.B, dqi.H, dqi.S))
-    return fail(SDPA_ERR_WORKSPACE, "workspace is smaller than sdpa_bwd_workspace_size()");
+  if (use_scratch) {
+    if (bwd_workspace_bytes(dqi.B, dqi.H, dqi.S) > kScratchBytes)
+      return fail(SDPA_ERR_UNSUPPORTED,
+                  "the allocation-free backward holds scratch for %zu query rows (B*H*Sq); "
+                  "this call has %lld: use sdpa_bwd_ext with a workspace",
+                  kScratchBytes / 8u, (long long)(dqi.B * dqi.H * dqi.S));
+  } else {
+    if (workspace == nullptr) return fail(SDPA_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(SDPA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < bwd_workspace_bytes(dqi.B, dqi.H, dqi.S))
+      return fail(SDPA_ERR_WORKSPACE, "workspace is smaller than sdpa_bwd_workspace_size()");
+  }
   Ext e;
   for (const Desc* d : {&ddo, &dki, &dvi, &dout_i, &dqo, &dko, &dvo})
     if (d->dtype != dqi.dtype)
@@ -453,6 +530,11 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (forced_launch_failure("backward launch")) return SDPA_ERR_HIP;
+  if (use_scratch) {
+    void* ptr = nullptr;
+    if ((rc = scratch_address(&ptr))) return rc;
+    p.dl = static_cast<float*>(ptr);
+  }
   (void)hipGetLastError();
   const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
                                       [&] {
@@ -461,6 +543,10 @@ int sdpa_bwd_ext(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tenso
                                       });
   return hip_status(err, "backward launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t sdpa_keep_bits_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
   if (B <= 0 || H <= 0 || Sq <= 0 || Sk <= 0) return 0;
