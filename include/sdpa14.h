@@ -40,9 +40,14 @@
  * Tensors: logical shape [B, H, S, E] with arbitrary element strides for the
  * first three dimensions and unit stride for E.  This covers both stride orders
  * of the nvFuser test: BHSE (memory [b, h, s, e]) and BSHE (memory [b, s, h, e]).
- * Supported now: dtype bf16 or fp16 (IEEE half; one per call), E in {64, 128};
- * data pointers 16-byte aligned and the first three strides multiples of 8
- * elements.
+ * Supported now: dtype bf16 or fp16 (IEEE half; one per call); any head dim E
+ * that is a multiple of 8 up to 128 (flash kernels commonly take a few fixed
+ * head dims; nvFuser issue 2278 notes that Flash Attention does not cover every
+ * input, and these calls do not fall back to another path); data pointers
+ * 16-byte aligned and the first three strides multiples of 8 elements.  Head
+ * dims below 64 run in the head-dim-64 kernels and those between 64 and 128 in
+ * the head-dim-128 kernels, with the missing columns read as zeros, so they
+ * cost as much as the larger size.
  *
  * Memory: every buffer is owned by the caller and lives on the current HIP
  * device; the library never allocates or frees device memory.  All work is

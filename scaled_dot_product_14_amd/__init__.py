@@ -6,7 +6,8 @@ declared in ``include/sdpa14.h``); this package is its thin Python binding.
     out, lse, seed, offset = sdpa_fwd(q, k, v, dropout_p, is_causal, scale)
     dq, dk, dv = sdpa_bwd(dout, q, k, v, out, lse, dropout_p, is_causal, seed, offset, scale)
 
-Tensors are bf16, logical [B, H, S, E], BHSE or BSHE stride order, E in {64, 128}.
+Tensors are bf16 or fp16, logical [B, H, S, E], BHSE or BSHE stride order, E a
+multiple of 8 up to 128.
 ``sdpa_fwd_ext`` / ``sdpa_bwd_ext`` add head sharding of the dropout stream and
 a device-resident RNG state for captured graphs.
 """

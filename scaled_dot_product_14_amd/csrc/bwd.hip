@@ -158,8 +158,8 @@ __device__ __forceinline__ void exchange_put(const f32x16 (&acc)[E / 32], float*
 template <int E, bool F16>
 __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], float mul,
                                                 uint16_t* dst, int64_t stride, int row0,
-                                                int limit, const float* red, int partner_slot,
-                                                bool upper, int lane) {
+                                                int limit, int e_real, const float* red,
+                                                int partner_slot, bool upper, int lane) {
   constexpr int HALF = E / 64;
   const f32x4* buf = reinterpret_cast<const f32x4*>(red + partner_slot * (HALF * 16 * 64));
   const int row = row0 + (lane & 31);
@@ -171,7 +171,9 @@ __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], flo
 #pragma unroll
     for (int cg = 0; cg < 4; ++cg) {
       const f32x4 o = buf[(i * 4 + cg) * 64 + lane];
-      *reinterpret_cast<uint2*>(dst + (int64_t)row * stride + eb * 32 + 8 * cg + 4 * g) =
+      const int e = eb * 32 + 8 * cg + 4 * g;
+      if (e >= e_real) continue;  // a column past the tensors' head dim
+      *reinterpret_cast<uint2*>(dst + (int64_t)row * stride + e) =
           pack16x4<F16>((acc[eb][4 * cg + 0] + o[0]) * mul, (acc[eb][4 * cg + 1] + o[1]) * mul,
                       (acc[eb][4 * cg + 2] + o[2]) * mul, (acc[eb][4 * cg + 3] + o[3]) * mul);
     }
@@ -198,14 +200,14 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   if (DROPOUT) load_dropout_state(drop);
   const int bhg = dropout_head(drop, b, h);
 
-  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, E);
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, p.E);
   const __amdgpu_buffer_rsrc_t rdo =
-      rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, E);
+      rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, p.E);
   // Waves 0, 1 stage rows of -D, waves 2, 3 rows of L (workspace planes).
   const __amdgpu_buffer_rsrc_t rdl = make_rsrc(
       p.dl + (wave >> 1) * ((int64_t)p.B * p.H * p.Sq) + (int64_t)bh * p.Sq, (uint32_t)p.Sq * 4u);
-  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
-  const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, p.E);
+  const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, p.E);
 
   f32x16 dva[NEB], dka[NEB];
 #pragma unroll
@@ -241,8 +243,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   uint32_t oq[NLD], odo[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) {
-    oq[k] = dma_src_offset<E>(k, tid, p.sq.s);
-    odo[k] = dma_src_offset<E>(k, tid, p.sdo.s);
+    oq[k] = dma_src_offset_e<E>(k, tid, p.sq.s, p.E);
+    odo[k] = dma_src_offset_e<E>(k, tid, p.sdo.s, p.E);
   }
   // Load idx (0 .. NPAIR_A-1) of stage it: (half, tensor, k) for the Q and dO
   // tiles, then -D (waves 0, 1) and L (waves 2, 3) of the pair's 64 rows, then
@@ -308,8 +310,8 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     uint32_t okv[NLD], ovv[NLD];
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
-      okv[k] = dma_src_offset<E>(k, tid, p.sk.s);
-      ovv[k] = dma_src_offset<E>(k, tid, p.sv.s);
+      okv[k] = dma_src_offset_e<E>(k, tid, p.sk.s, p.E);
+      ovv[k] = dma_src_offset_e<E>(k, tid, p.sv.s, p.E);
     }
     issue_tiles<E>(lds + 2 * C::STAGE_A, wave, (uint32_t)kb0, rk, (uint32_t)(p.sk.s * 2), okv, rvv,
                    (uint32_t)(p.sv.s * 2), ovv);
@@ -446,8 +448,9 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   uint16_t* dvp = p.dv + b * p.sdv.b + h * p.sdv.h;
   uint16_t* dkp = p.dk + b * p.sdk.b + h * p.sdk.h;
   const int partner = 4 * sb + 2 * (1 - qs);
-  exchange_finish<E, F16>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, red, partner + 0, upper, lane);
-  exchange_finish<E, F16>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, red, partner + 1, upper, lane);
+  exchange_finish<E, F16>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, p.E, red, partner + 0, upper,
+                          lane);
+  exchange_finish<E, F16>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, p.E, red, partner + 1, upper, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -465,11 +468,11 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   const int qrow = q0 + l32;
   const float c = p.scale_log2;
 
-  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, E);
+  const __amdgpu_buffer_rsrc_t rq = rows_rsrc(p.q + b * p.sq.b + h * p.sq.h, p.Sq, p.sq.s, p.E);
   const __amdgpu_buffer_rsrc_t rdo =
-      rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, E);
-  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, E);
-  const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, E);
+      rows_rsrc(p.dout + b * p.sdo.b + h * p.sdo.h, p.Sq, p.sdo.s, p.E);
+  const __amdgpu_buffer_rsrc_t rk = rows_rsrc(p.k + b * p.sk.b + h * p.sk.h, p.Sk, p.sk.s, p.E);
+  const __amdgpu_buffer_rsrc_t rvv = rows_rsrc(p.v + b * p.sv.b + h * p.sv.h, p.Sk, p.sv.s, p.E);
 
   // Waves 0, 1 stage rows of -D, waves 2, 3 rows of L (workspace planes).
   const __amdgpu_buffer_rsrc_t rdl = make_rsrc(
@@ -507,8 +510,8 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   uint32_t okk[NLD], ov[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) {
-    okk[k] = dma_src_offset<E>(k, tid, p.sk.s);
-    ov[k] = dma_src_offset<E>(k, tid, p.sv.s);
+    okk[k] = dma_src_offset_e<E>(k, tid, p.sk.s, p.E);
+    ov[k] = dma_src_offset_e<E>(k, tid, p.sv.s, p.E);
   }
   // Load idx (0 .. NPAIR_B-1) of stage it: (half, tensor, k) for the K and V
   // tiles, then the two loads of the bias block.
@@ -571,8 +574,8 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     uint32_t oqq[NLD], odd[NLD];
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
-      oqq[k] = dma_src_offset<E>(k, tid, p.sq.s);
-      odd[k] = dma_src_offset<E>(k, tid, p.sdo.s);
+      oqq[k] = dma_src_offset_e<E>(k, tid, p.sq.s, p.E);
+      odd[k] = dma_src_offset_e<E>(k, tid, p.sdo.s, p.E);
     }
     issue_tiles<E>(lds + 2 * C::STAGE_B, wave, (uint32_t)q0b, rq, (uint32_t)(p.sq.s * 2), oqq, rdo,
                    (uint32_t)(p.sdo.s * 2), odd);
@@ -700,7 +703,8 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   exchange_put<E>(dqa, red, 2 * qsb + ks, upper, lane);
   ring_barrier<0>();
   uint16_t* dqp = p.dq + b * p.sdq.b + h * p.sdq.h;
-  exchange_finish<E, F16>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, red, 2 * qsb + (1 - ks), upper, lane);
+  exchange_finish<E, F16>(dqa, 1.f, dqp, p.sdq.s, q0, p.Sq, p.E, red, 2 * qsb + (1 - ks), upper,
+                          lane);
 }
 
 // Order in which a head's dK/dV and dQ blocks are dealt out: longest estimated
@@ -770,7 +774,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, uint32_t nbl
     const int i = (int)(v - bh * nblk) * RPB + tid / CPR;
     const uint32_t b = bh / (uint32_t)p.H, h = bh - b * (uint32_t)p.H;
     float d = 0.f;
-    if (i < p.Sq) {
+    if (i < p.Sq && col * 8 < p.E) {
       const bf16x8 x = load_bf16x8(p.dout + b * p.sdo.b + h * p.sdo.h + i * p.sdo.s + col * 8);
       const bf16x8 y = load_bf16x8(p.o + b * p.so.b + h * p.so.h + i * p.so.s + col * 8);
       d = dot8_16<F16>(x, y, 0.f);
@@ -859,8 +863,9 @@ size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   return (raw + 255u) & ~(size_t)255u;
 }
 
-hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, bool f16,
+hipError_t launch_bwd(const BwdParams& p, bool causal, bool dropout, bool f16,
                       hipStream_t stream) {
+  const int E = tile_head_dim(p.E);
   if (f16)
     return E == 64 ? launch_bwd_t<64, true>(p, causal, dropout, stream)
                    : launch_bwd_t<128, true>(p, causal, dropout, stream);

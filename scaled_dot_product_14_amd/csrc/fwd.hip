@@ -43,11 +43,10 @@
 // causal tile then waits a little before its first loads (longer the fewer
 // steps it has), so that the heaviest tiles, which set the kernel's length,
 // are served first.
-#include <atomic>
-
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_ring.h"
+#include "occupancy.h"
 
 namespace sdpa14 {
 namespace {
@@ -151,12 +150,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
   // Q as the B operand of S^T = K Q^T: lane holds its row, e = 16*es + 8*g + 0..7.
   // Rows past Sq read as zeros through the buffer range check.
   const __amdgpu_buffer_rsrc_t qr =
-      make_rsrc(qp, (uint32_t)(((int64_t)(p.Sq - 1) * p.sq.s + E) * 2));
+      make_rsrc(qp, (uint32_t)(((int64_t)(p.Sq - 1) * p.sq.s + p.E) * 2));
   bf16x8 qf[NES];
 #pragma unroll
   for (int es = 0; es < NES; ++es)
     qf[es] = __builtin_bit_cast(
-        bf16x8, buffer_load16(qr, (uint32_t)(((int64_t)qrow * p.sq.s + es * 16 + 8 * g) * 2)));
+        bf16x8, buffer_load16(qr, (uint32_t)(((int64_t)qrow * p.sq.s + es * 16 + 8 * g) * 2) |
+                                      (es * 16 + 8 * g < p.E ? 0u : 0x80000000u)));
 
   // Additive bias.  The wave's 32 rows x BN keys of tile t are fetched one step
   // ahead with row-contiguous loads (lane l: row 16*i + l/4 of the wave's rows,
@@ -184,16 +184,16 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
 
   // K and V rows past kend read as zeros.  Stage it % NSTAGE of the ring holds
   // key rows it*ROWS .. it*ROWS + ROWS-1, loaded straight into LDS.
-  const uint32_t kbytes = (uint32_t)(((int64_t)(kend - 1) * p.sk.s + E) * 2);
-  const uint32_t vbytes = (uint32_t)(((int64_t)(kend - 1) * p.sv.s + E) * 2);
+  const uint32_t kbytes = (uint32_t)(((int64_t)(kend - 1) * p.sk.s + p.E) * 2);
+  const uint32_t vbytes = (uint32_t)(((int64_t)(kend - 1) * p.sv.s + p.E) * 2);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(kp, kend > 0 ? kbytes : 0);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(vp, kend > 0 ? vbytes : 0);
   const uint32_t kstride = (uint32_t)(p.sk.s * 2), vstride = (uint32_t)(p.sv.s * 2);
   uint32_t ok[NLD], ov[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) {
-    ok[k] = dma_src_offset<E, NT>(k, tid, p.sk.s);
-    ov[k] = dma_src_offset<E, NT>(k, tid, p.sv.s);
+    ok[k] = dma_src_offset_e<E, NT>(k, tid, p.sk.s, p.E);
+    ov[k] = dma_src_offset_e<E, NT>(k, tid, p.sv.s, p.E);
   }
   auto stage = [&](int it) { return lds + ring_offset<STAGE, NSTAGE>(it); };
   auto issue = [&](int it) {
@@ -432,7 +432,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
 #pragma unroll
       for (int cg = 0; cg < 4; ++cg) {
         const int e = eb * 32 + 8 * cg + 4 * g;
-        *reinterpret_cast<uint2*>(op + e) =
+        if (e < p.E)
+          *reinterpret_cast<uint2*>(op + e) =
             pack16x4<F16>(oacc[eb][4 * cg + 0] * inv, oacc[eb][4 * cg + 1] * inv,
                         oacc[eb][4 * cg + 2] * inv, oacc[eb][4 * cg + 3] * inv);
       }
@@ -488,32 +489,6 @@ __global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy
     fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16>(p, bh, qt, causal_steps_max(p, light_rows, 64, 2),
                                                     hold, lds);
   }
-}
-
-// Compute units of the current device, looked up once per device.
-int device_cus() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
-// Workgroups of kernel K resident per compute unit (queried once per kernel).
-template <auto K>
-int resident_per_cu(int threads) {
-  static std::atomic<int> cache{-1};
-  int n = cache.load(std::memory_order_relaxed);
-  if (n < 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, K, threads, 0) != hipSuccess) n = 0;
-    cache.store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 constexpr int kHoldSteps = 4;  // longest start-up hold, in steps of slack
@@ -606,8 +581,9 @@ bool split_fits(const FwdParams& p) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool f16,
+hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
                       const TileChoice& tiles, hipStream_t stream) {
+  const int E = tile_head_dim(p.E);
   // Shape: 4 query sub-tiles sharing each key tile when there are enough
   // 128-row tiles to give every compute unit two workgroups; otherwise two
   // query sub-tiles with the keys split in two, for a shorter critical path.

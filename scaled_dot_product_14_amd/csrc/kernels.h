@@ -22,6 +22,8 @@ struct FwdParams {
   float* lse;  // contiguous [B, H, Sq], or null (inference: not written)
   Strides sq, sk, sv, so;
   int B, H, Sq, Sk;
+  int E;             // head dim of the tensors, at most the kernel's tile head dim;
+                     // columns past it read as zeros and are never stored
   float scale_log2;  // scale * log2(e)
   DropoutParams drop;
   const uint16_t* bias;  // additive bias [B, H, Sq, Sk] (bf16 bits, unit key stride), or null
@@ -43,6 +45,7 @@ struct BwdParams {
   float* dl;         // workspace: -D_i plane then LSE_i*log2(e) - log2(scale) plane, each [B, H, Sq]
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, Sq, Sk;
+  int E;             // head dim of the tensors (as in FwdParams)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   DropoutParams drop;
@@ -65,12 +68,15 @@ struct TileChoice {
                   // 4 = causal split launch (kinds 3 with 32-key tiles and 2, head dim 64)
 };
 
-// f16: the 16-bit tensors are IEEE half instead of bfloat16.
-hipError_t launch_fwd(const FwdParams& p, int E, bool causal, bool dropout, bool f16,
+// Tile head dim of the kernels that run head dim E (a multiple of 8, at most 128).
+inline int tile_head_dim(int E) { return E <= 64 ? 64 : 128; }
+// f16: the 16-bit tensors are IEEE half instead of bfloat16.  p.E is the head
+// dim; the kernels run at tile_head_dim(p.E).
+hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
                       const TileChoice& tiles, hipStream_t stream);
 // Backward: a row pass filling p.dl, then the main kernel.  p.dl must hold
 // bwd_workspace_bytes(B, H, Sq) bytes.
-hipError_t launch_bwd(const BwdParams& p, int E, bool causal, bool dropout, bool f16,
+hipError_t launch_bwd(const BwdParams& p, bool causal, bool dropout, bool f16,
                       hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 // Words per row of the keep-bit cache: bit j % 32 of word j / 32 is key j's bit.

@@ -82,6 +82,21 @@ __device__ __forceinline__ uint32_t dma_src_offset(int k, int tid, int64_t row_s
   return (uint32_t)row * (uint32_t)(row_stride * 2) + (uint32_t)((pos ^ tile_swz<E>(row)) * 16);
 }
 
+// The same offset for a tile whose rows hold only the first e_real of their E
+// elements (e_real a multiple of 8): a chunk past e_real gets bit 31 set.  A
+// (batch, head) slice stays below 2 GiB, so the buffer range check turns that
+// load into zeros, and adding a row offset below 2^31 keeps the bit.
+template <int E, int NT = 256>
+__device__ __forceinline__ uint32_t dma_src_offset_e(int k, int tid, int64_t row_stride,
+                                                     int e_real) {
+  constexpr int CPR = E / 8;
+  const int slot = k * NT + tid;
+  const int row = slot / CPR, pos = slot % CPR;
+  const int chunk = pos ^ tile_swz<E>(row);
+  return ((uint32_t)row * (uint32_t)(row_stride * 2) + (uint32_t)(chunk * 16)) |
+         (chunk * 8 < e_real ? 0u : 0x80000000u);
+}
+
 // LDS byte offset, within a tile, of the chunk holding elements 8c .. 8c+7 of row r.
 template <int E>
 __device__ __forceinline__ int chunk_off(int r, int c) {

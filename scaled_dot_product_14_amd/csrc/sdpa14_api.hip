@@ -107,9 +107,9 @@ int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
   if (q.E != k.E) return fail(SDPA_ERR_INVALID, "q and k have different head dims");
   if (v.E != q.E) return fail(SDPA_ERR_INVALID, "value head dim Ev = %lld differs from E = %lld",
                               (long long)v.E, (long long)q.E);
-  if (q.E != 64 && q.E != 128)
-    return fail(SDPA_ERR_UNSUPPORTED, "head dim %lld is not supported (64 or 128)",
-                (long long)q.E);
+  if (q.E % 8 != 0 || q.E > 128)
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "head dim %lld is not supported (a multiple of 8, at most 128)", (long long)q.E);
   const int64_t grid_f = q.B * q.H * ((q.S + 31) / 32 + (k.S + 31) / 32);
   if (grid_f > kMaxGrid) return fail(SDPA_ERR_UNSUPPORTED, "problem too large for one launch");
   if (!slice_ok(q) || !slice_ok(k) || !slice_ok(v))
@@ -397,6 +397,7 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   p.H = (int)dq.H;
   p.Sq = (int)dq.S;
   p.Sk = (int)dk.S;
+  p.E = (int)dq.E;
   p.scale_log2 = sc * 1.44269504088896340736f;
   p.drop = make_dropout(dropout_p, s0, o0, e.heads_total, e.head_offset, e.rng_used);
   p.bias = e.bias;
@@ -404,7 +405,7 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
   p.keep = drop ? e.keep_bits : nullptr;
   p.keep_w = keep_words(dk.S);
   const hipError_t err = timed_launch(SDPA_KERNEL_FWD, st, [&] {
-    return launch_fwd(p, (int)dq.E, is_causal != 0, drop, dq.dtype == SDPA_F16, tile_choice(),
+    return launch_fwd(p, is_causal != 0, drop, dq.dtype == SDPA_F16, tile_choice(),
                       st);
   });
   if (err != hipSuccess) undo_advance();
@@ -519,6 +520,7 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   p.H = (int)dqi.H;
   p.Sq = (int)dqi.S;
   p.Sk = (int)dki.S;
+  p.E = (int)dqi.E;
   p.scale = sc;
   p.scale_log2 = sc * 1.44269504088896340736f;
   p.drop = make_dropout(dropout_p, seed, offset, e.heads_total, e.head_offset, e.rng_used);
@@ -526,7 +528,6 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   p.sbias = e.sbias;
   p.keep = dropout_p > 0.0 ? e.keep_bits : nullptr;
   p.keep_w = keep_words(dki.S);
-  const int E = (int)dqi.E;
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (forced_launch_failure("backward launch")) return SDPA_ERR_HIP;
@@ -538,7 +539,7 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   (void)hipGetLastError();
   const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
                                       [&] {
-                                        return launch_bwd(p, E, causal, drop,
+                                        return launch_bwd(p, causal, drop,
                                                           dqi.dtype == SDPA_F16, st);
                                       });
   return hip_status(err, "backward launch");

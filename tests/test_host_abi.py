@@ -85,7 +85,13 @@ def _err(lib):
     (dict(q=_t(dtype=2)), bnd.SDPA_ERR_UNSUPPORTED, "dtype"),
     (dict(q=_t(dtype=1)), bnd.SDPA_ERR_INVALID, "one dtype"),
     (dict(q=_t(dtype=1), k=_t(dtype=1), v=_t(dtype=1)), bnd.SDPA_ERR_INVALID, "one dtype"),
-    (dict(q=_t(E=32), k=_t(E=32), v=_t(E=32), out=_t(E=32)), bnd.SDPA_ERR_UNSUPPORTED, "head dim"),
+    (dict(q=_t(E=136), k=_t(E=136), v=_t(E=136), out=_t(E=136)), bnd.SDPA_ERR_UNSUPPORTED,
+     "head dim"),
+    (dict(q=_t(E=12, stride=(2 * 128 * 16, 128 * 16, 16, 1)),
+          k=_t(E=12, stride=(2 * 128 * 16, 128 * 16, 16, 1)),
+          v=_t(E=12, stride=(2 * 128 * 16, 128 * 16, 16, 1)),
+          out=_t(E=12, stride=(2 * 128 * 16, 128 * 16, 16, 1))), bnd.SDPA_ERR_UNSUPPORTED,
+     "multiple of 8"),
     (dict(q=_t(stride=(2 * 128 * 64, 128 * 64, 1, 128))), bnd.SDPA_ERR_UNSUPPORTED, "stride"),
     (dict(q=_t(stride=(2 * 128 * 68, 128 * 68, 68, 1))), bnd.SDPA_ERR_UNSUPPORTED, "multiple of 8"),
     (dict(q=_t(data=FAKE + 8)), bnd.SDPA_ERR_UNSUPPORTED, "aligned"),
