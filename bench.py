@@ -67,8 +67,9 @@ def log(msg):
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
-    "fwd": ["fwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h"],
-    "bwd": ["bwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h"],
+    "fwd": ["fwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h", "occupancy.h"],
+    "bwd_main": ["bwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h"],
+    "bwd_rows": ["bwd.hip", "device_common.h", "kernels.h"],
 }
 
 
@@ -235,14 +236,15 @@ def main():
                                            lse=lse, bias=bias, keep_bits=keep)
         state["so"] = (s, o)
 
-    def bwd():
+    def bwd(parts=0):
         s, o = state["so"]
-        if bias is None and keep is None:
+        if bias is None and keep is None and parts == 0:
             sdpa.sdpa_bwd(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
                           dk=dk, dv=dv, workspace=ws)
         else:
             sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
-                              dk=dk, dv=dv, workspace=ws, bias=bias, keep_bits=keep)
+                              dk=dk, dv=dv, workspace=ws, bias=bias, keep_bits=keep,
+                              bwd_parts=parts)
 
     def step():
         fwd()
@@ -284,15 +286,31 @@ def main():
     ms_fwd_eager = timed_loop(fwd, args.steps)
     ms_bwd_eager = timed_loop(bwd, args.steps)
     log(f"eager launches: fwd {ms_fwd_eager * 1e3:.2f} us, bwd {ms_bwd_eager * 1e3:.2f} us")
+    # The backward's two kernels on their own: event pairs the library records
+    # around each launch, captured as graph nodes in a graph of back-to-back
+    # backward calls.
+    ms_rows = replayed_launches(lambda: bwd(parts=1), per_graph, args.steps)
+    ms_main = replayed_launches(lambda: bwd(parts=2), per_graph, args.steps)
+    n_main = n_rows = per_graph * max(1, args.steps // per_graph)
+    log(f"graph-replayed backward kernels: row pass {ms_rows * 1e3:.2f} us, "
+        f"main {ms_main * 1e3:.2f} us")
+    rows_bytes = w.B * w.H * w.Sq * (4 * w.E + 12)  # dO, O (bf16) and LSE read; -D, L written
     kern = {"fwd": {"avg_us": ms_fwd * 1e3, "launches": per_graph * max(1, args.steps // per_graph),
                     "timing": "graph of back-to-back forward calls, events on the launch stream"},
-            "bwd": {"avg_us": ms_bwd * 1e3, "launches": per_graph * max(1, args.steps // per_graph),
-                    "timing": "graph of back-to-back backward calls (row pass + main kernel), "
-                              "events on the launch stream"}}
+            "bwd_main": {"avg_us": ms_main * 1e3, "launches": n_main,
+                         "timing": "graph of back-to-back main-kernel launches (backward calls "
+                                   "with bwd_parts = 2 on a filled workspace), events on the "
+                                   "launch stream"},
+            "bwd_rows": {"avg_us": ms_rows * 1e3, "launches": n_rows,
+                         "timing": "graph of back-to-back row passes (bwd_parts = 1), events "
+                                   "on the launch stream",
+                         "algorithmic_bytes": rows_bytes,
+                         "GBps": rows_bytes / (ms_rows * 1e-3) / 1e9,
+                         "frac_hbm_peak": rows_bytes / (ms_rows * 1e-3) / 1e9 / PEAK_HBM_GBS}}
 
     # Per-launch brackets: events recorded by the library around each of its
     # launches (their own cost, ~1-2 us per launch, is inside the figure).
-    names = {sdpa.KERNEL_FWD: "fwd", sdpa.KERNEL_BWD: "bwd"}
+    names = {sdpa.KERNEL_FWD: "fwd", sdpa.KERNEL_BWD: "bwd_main", sdpa.KERNEL_BWD_ROWS: "bwd_rows"}
     for kind in names:
         sdpa.sdpa_profile_read(kind)
     sdpa.sdpa_profile_enable(True)
@@ -336,18 +354,22 @@ def main():
             cold[name + "_avg_us"] = tot / max(n, 1) * 1e3
         del sets
         log(f"cold-cache kernel averages (us): fwd {cold['fwd_avg_us']:.2f}, "
-            f"bwd {cold['bwd_avg_us']:.2f} over {n_sets} input sets")
+            f"bwd main {cold['bwd_main_avg_us']:.2f}, row pass {cold['bwd_rows_avg_us']:.2f} "
+            f"over {n_sets} input sets")
 
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
     kern["fwd"]["algorithmic_tflop"] = f_fwd / 1e12
-    kern["bwd"]["algorithmic_tflop"] = f_bwd / 1e12
-    for name in ("fwd", "bwd"):
+    kern["bwd_main"]["algorithmic_tflop"] = f_bwd / 1e12  # the row pass has no products
+    for name in ("fwd", "bwd_main"):
         kk = kern[name]
         kk["tflops"] = kk["algorithmic_tflop"] / (kk["avg_us"] * 1e-6)
         kk["frac_peak"] = kk["tflops"] / PEAK_BF16_TFLOPS
-    dominant = max(kern, key=lambda n: kern[n]["avg_us"])
+    # The dominant kernel: the one of the two contraction kernels with the
+    # longest launch (the backward main kernel at every workload measured).
+    dominant = max(("fwd", "bwd_main"), key=lambda n: kern[n]["avg_us"])
     dk_ = kern[dominant]
-    roof = {"kernel": dominant, "bound": "mfma", "achieved": dk_["tflops"],
+    names_k = {"fwd": "forward kernel", "bwd_main": "backward main kernel (bwd_kernel)"}
+    roof = {"kernel": names_k[dominant], "bound": "mfma", "achieved": dk_["tflops"],
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dk_["frac_peak"],
             "traffic": measured_traffic(w.name, dominant) if bias is None and keep is None else None}
 

@@ -183,6 +183,13 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       backward given the same buffer reads them instead of regenerating the
  *       Philox stream in each of its two workgroup roles.  The buffer must
  *       come from the forward with the same inputs, seed and offset, unchanged.
+ *   bwd_parts  (backward only; 0 means both)
+ *       Which of the backward's two kernels to enqueue: 1 the row pass alone
+ *       (D = rowsum(dout * out) and the base-2 LSE into the workspace), 2 the
+ *       main kernel alone (dq, dk, dv from a workspace that a row pass of the
+ *       same dout, out, lse and scale filled earlier in stream order), 3 or 0
+ *       both.  Lets a caller overlap the row pass with other work and time the
+ *       two kernels apart; the arguments are validated in full either way.
  */
 typedef struct sdpa_ext {
   int64_t head_offset;
@@ -191,6 +198,7 @@ typedef struct sdpa_ext {
   uint64_t* rng_used;
   const sdpa_tensor* bias;
   uint32_t* keep_bits;
+  int32_t bwd_parts;
 } sdpa_ext;
 
 /* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL.
@@ -258,13 +266,20 @@ int sdpa_debug_dropout_mask(uint64_t seed, uint64_t offset, double dropout_p,
 
 /*
  * Kernel timing by HIP events, for measurement.  While enabled, every kernel
- * the library launches is bracketed by a pair of events on its own stream.
- * sdpa_profile_read waits for the recorded events, returns the summed duration
- * (ms) and launch count of one kernel kind since the last read, and clears
- * that kind.  Kinds: 0 forward kernel, 1 backward kernel.  At most 8192
- * launches are kept per kind; further launches are not timed.
+ * the library launches is bracketed by a pair of events on its own stream
+ * (also inside a captured graph: the pairs then time the launches of the
+ * latest replay).  sdpa_profile_read waits for the recorded events, returns
+ * the summed duration (ms) and launch count of one kernel kind since the last
+ * read, and clears that kind.  Kinds: 0 forward kernel, 1 backward main
+ * kernel, 2 backward row pass.  At most 8192 launches are kept per kind;
+ * further launches are not timed.
  */
-enum { SDPA_KERNEL_FWD = 0, SDPA_KERNEL_BWD = 1, SDPA_KERNEL_KINDS = 2 };
+enum {
+  SDPA_KERNEL_FWD = 0,
+  SDPA_KERNEL_BWD = 1,
+  SDPA_KERNEL_BWD_ROWS = 2,
+  SDPA_KERNEL_KINDS = 3
+};
 int sdpa_profile_enable(int on);
 int sdpa_profile_read(int kind, double* total_ms, int64_t* launches);
 

@@ -15,6 +15,7 @@ a device-resident RNG state for captured graphs.
 from ._binding import (  # noqa: F401
     EXPORTED,
     KERNEL_BWD,
+    KERNEL_BWD_ROWS,
     KERNEL_FWD,
     LIB_PATH,
     SdpaError,

@@ -25,7 +25,8 @@ SDPA_BF16 = 0
 SDPA_F16 = 1
 
 KERNEL_FWD = 0
-KERNEL_BWD = 1
+KERNEL_BWD = 1       # backward main kernel
+KERNEL_BWD_ROWS = 2  # backward row pass
 
 EXPORTED = (
     "sdpa_fwd", "sdpa_bwd", "sdpa_fwd_ext", "sdpa_bwd_ext", "sdpa_bwd_workspace_size",
@@ -54,6 +55,7 @@ class SdpaExt(ctypes.Structure):
         ("rng_used", ctypes.c_void_p),
         ("bias", ctypes.POINTER(SdpaTensor)),
         ("keep_bits", ctypes.c_void_p),
+        ("bwd_parts", ctypes.c_int32),
     ]
 
 
@@ -259,9 +261,10 @@ def sdpa_keep_bits_size(B: int, H: int, Sq: int, Sk: int) -> int:
 
 
 def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None, keep_bits=None,
-         device=None):
+         device=None, bwd_parts=0):
     """The options block and the objects it points into (keep both alive for the call)."""
     e = SdpaExt()
+    e.bwd_parts = int(bwd_parts)
     if keep_bits is not None:
         _on_device(keep_bits, device, "keep_bits")
         if not keep_bits.is_contiguous():
@@ -328,11 +331,13 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
 def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int = 0,
                  offset: int = 0, scale=None, dq=None, dk=None, dv=None, workspace=None, *,
                  head_offset: int = 0, heads_total: int = 0, rng_used=None, bias=None,
-                 keep_bits=None):
+                 keep_bits=None, bwd_parts: int = 0):
     """Backward with options (see ``sdpa_fwd_ext``): returns ``(dq, dk, dv)``.
 
     With ``rng_used`` the kernels read (seed, offset) from that device tensor
-    and ``seed`` / ``offset`` are ignored.
+    and ``seed`` / ``offset`` are ignored.  ``bwd_parts`` picks the kernels to
+    enqueue: 1 the row pass (fills ``workspace``), 2 the main kernel (reads a
+    workspace a row pass filled), 0 or 3 both.
     """
     lib = load_library()
     _on_device(q, None, "q")
@@ -348,7 +353,8 @@ def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, see
     descs = [describe(t, q.device, n) for t, n in zip(
         (dout, q, k, v, out, dq, dk, dv), ("dout", "q", "k", "v", "out", "dq", "dk", "dv"))]
     ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
-                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device)
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device,
+                      bwd_parts)
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd_ext(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                               float(dropout_p), int(bool(is_causal)), int(seed), int(offset),

@@ -789,13 +789,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, uint32_t nbl
 }
 
 template <int E, bool F16>
-hipError_t launch_bwd_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
+hipError_t launch_rows_t(const BwdParams& p, hipStream_t stream) {
   constexpr int RPB = 256 / (E / 8);
   // B*H*nblk < 2^32: B*H*ceil(Sq/32) is below 2^31 and RPB >= 16.
   const uint32_t nblk = (uint32_t)((p.Sq + RPB - 1) / RPB);
   const uint32_t total = (uint32_t)((int64_t)p.B * p.H * nblk);
   hipLaunchKernelGGL((bwd_prep_kernel<E, F16>), dim3(std::min(total, 1u << 20)), dim3(256), 0,
                      stream, p, nblk, total);
+  return hipGetLastError();
+}
+
+template <int E, bool F16>
+hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
   BwdOrder ord;
@@ -863,14 +868,20 @@ size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   return (raw + 255u) & ~(size_t)255u;
 }
 
-hipError_t launch_bwd(const BwdParams& p, bool causal, bool dropout, bool f16,
-                      hipStream_t stream) {
+hipError_t launch_bwd_rows(const BwdParams& p, bool f16, hipStream_t stream) {
+  const int E = tile_head_dim(p.E);
+  if (f16) return E == 64 ? launch_rows_t<64, true>(p, stream) : launch_rows_t<128, true>(p, stream);
+  return E == 64 ? launch_rows_t<64, false>(p, stream) : launch_rows_t<128, false>(p, stream);
+}
+
+hipError_t launch_bwd_main(const BwdParams& p, bool causal, bool dropout, bool f16,
+                           hipStream_t stream) {
   const int E = tile_head_dim(p.E);
   if (f16)
-    return E == 64 ? launch_bwd_t<64, true>(p, causal, dropout, stream)
-                   : launch_bwd_t<128, true>(p, causal, dropout, stream);
-  return E == 64 ? launch_bwd_t<64, false>(p, causal, dropout, stream)
-                 : launch_bwd_t<128, false>(p, causal, dropout, stream);
+    return E == 64 ? launch_main_t<64, true>(p, causal, dropout, stream)
+                   : launch_main_t<128, true>(p, causal, dropout, stream);
+  return E == 64 ? launch_main_t<64, false>(p, causal, dropout, stream)
+                 : launch_main_t<128, false>(p, causal, dropout, stream);
 }
 
 }  // namespace sdpa14

@@ -23,10 +23,12 @@
 //                          over keys, four consecutive keys per register group.
 //   online softmax         every lane owns one query row; the row max needs one
 //                          exchange with lane l^32 (permlane32_swap).  The
-//                          reference max moves only when it grows by more than
-//                          2^8 (in the exp2 domain), so most tiles skip the
-//                          rescale of the O accumulator; probabilities then stay
-//                          below 2^8, harmless for fp32 sums and bf16 operands.
+//                          reference is lazy: the row maximum is taken only on a
+//                          row's first visible tile and when a tile's sum shows
+//                          that a probability may pass 2^16 (in the exp2
+//                          domain), so most tiles take no maximum and skip the
+//                          rescale of the O accumulator; probabilities stay
+//                          below 2^16, harmless for fp32 sums and bf16 operands.
 //   dropout                the four consecutive keys of a register group are
 //                          exactly one Philox call.
 //   O^T += V^T P^T         A = V^T read transposed from the row-major V tile
@@ -63,7 +65,7 @@ __device__ __forceinline__ uint32_t bias_bytes(const P& p) {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kRescaleSlack = 8.f;  // log2 units the reference max may lag
+constexpr float kLazyLimit = 65536.f;  // a lane's tile sum above this re-takes the row maximum
 
 // Maps a workgroup id to (head, rank); rank 0 is the heaviest query tile.
 __device__ __forceinline__ void wg_to_tile(int bid, int bh_count, int& bh, int& rank) {
@@ -306,43 +308,58 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
             if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -INFINITY;
       }
 
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
-      mx = pair_max(mx) * c;
-      // Move the reference max only when it grew by more than the slack; the
-      // decision is per row, the skip of the rescale is per wave.
-      const bool grow = mx > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? mx : m_run;
-        // A row that has seen only hidden keys (-inf bias entries) keeps
-        // m_run = -inf while another row of the wave grows: its sum and O are
-        // still zero, and -inf - -inf must not turn them into NaN.
-        const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[eb][r] *= alpha;
-      }
-
+      // Online softmax against a lazy reference: P = exp2(c*S - m) with the
+      // row's current reference m.  The row maximum is taken, and m raised to
+      // it with the sum and O rescaled, only for a row that has seen no visible
+      // key yet or whose tile sum shows that an exponential may pass 2^16 (NaN
+      // included); most tiles take no maximum.  Only the rows that ask move
+      // their reference, so a row's values never depend on the other rows of
+      // the wave.
       // P (bf16) as the B operand: 16-key step ksx takes registers 8*(ksx%2)..+7
       // of block ksx/2, i.e. keys 16*ksx + 8*(i/4) + 4*g + i%4 for element i.  The
       // row sum adds the fp32 probabilities (the log-sum-exp needs them unrounded).
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // never -inf - -inf
       bf16x8 pb[BN / 16];
       float rs = 0.f;
+      auto exps = [&](float m_use) {
+        rs = 0.f;
 #pragma unroll
-      for (int ksx = 0; ksx < BN / 16; ++ksx)
+        for (int ksx = 0; ksx < BN / 16; ++ksx)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], c, -m_use));
-          rs += pv;
-          pb[ksx][i] = to16<F16>(pv);
+          for (int i = 0; i < 8; ++i) {
+            const float pv = fast_exp2(fmaf(s[ksx >> 1][8 * (ksx & 1) + i], c, -m_use));
+            rs += pv;
+            pb[ksx][i] = to16<F16>(pv);
+          }
+      };
+      bool fresh = m_run == -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(!fresh)) {
+        exps(fresh ? 0.f : m_run);
+        fresh = fresh || !(rs <= kLazyLimit);
+        fresh = pair_or(fresh ? 1u : 0u) != 0u;  // both lanes of a row agree
+      }
+      if (__builtin_amdgcn_ballot_w64(fresh)) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+        mx = pair_max(mx) * c;
+        const bool grow = fresh && mx > m_run;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m_run;
+          // A row that has seen only hidden keys (-inf bias entries) keeps
+          // m_run = -inf while another row of the wave grows: its sum and O are
+          // still zero, and -inf - -inf must not turn them into NaN.
+          const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[eb][r] *= alpha;
         }
+        exps((m_run == -INFINITY) ? 0.f : m_run);  // never -inf - -inf
+      }
       l_run += rs;
 
       if (DROPOUT) {

@@ -74,10 +74,11 @@ inline int tile_head_dim(int E) { return E <= 64 ? 64 : 128; }
 // dim; the kernels run at tile_head_dim(p.E).
 hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
                       const TileChoice& tiles, hipStream_t stream);
-// Backward: a row pass filling p.dl, then the main kernel.  p.dl must hold
-// bwd_workspace_bytes(B, H, Sq) bytes.
-hipError_t launch_bwd(const BwdParams& p, bool causal, bool dropout, bool f16,
-                      hipStream_t stream);
+// Backward: the row pass filling p.dl (which must hold bwd_workspace_bytes(B,
+// H, Sq) bytes), then the main kernel, launched in that order on one stream.
+hipError_t launch_bwd_rows(const BwdParams& p, bool f16, hipStream_t stream);
+hipError_t launch_bwd_main(const BwdParams& p, bool causal, bool dropout, bool f16,
+                           hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 // Words per row of the keep-bit cache: bit j % 32 of word j / 32 is key j's bit.
 inline int keep_words(int64_t Sk) { return (int)(((Sk + 31) / 32 + 3) / 4 * 4); }

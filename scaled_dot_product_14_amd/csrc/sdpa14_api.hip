@@ -157,6 +157,7 @@ struct Ext {
   const uint16_t* bias = nullptr;
   Strides sbias{0, 0, 0};
   uint32_t* keep_bits = nullptr;
+  int bwd_parts = 3;  // bit 0: row pass, bit 1: main kernel
 };
 
 int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int dtype,
@@ -206,6 +207,11 @@ int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
       if (rc) return rc;
     }
     e.keep_bits = ext->keep_bits;
+    if (!forward) {
+      if (ext->bwd_parts < 0 || ext->bwd_parts > 3)
+        return fail(SDPA_ERR_INVALID, "bwd_parts = %d not in 0..3", ext->bwd_parts);
+      e.bwd_parts = ext->bwd_parts == 0 ? 3 : ext->bwd_parts;
+    }
     if (reinterpret_cast<uintptr_t>(e.keep_bits) % 16 != 0)
       return fail(SDPA_ERR_UNSUPPORTED, "keep_bits is not 16-byte aligned");
     if (e.keep_bits != nullptr && Sq * keep_words(Sk) * 4 >= (int64_t(1) << 32))
@@ -537,11 +543,13 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
     p.dl = static_cast<float*>(ptr);
   }
   (void)hipGetLastError();
-  const hipError_t err = timed_launch(SDPA_KERNEL_BWD, st,
-                                      [&] {
-                                        return launch_bwd(p, causal, drop,
-                                                          dqi.dtype == SDPA_F16, st);
-                                      });
+  const bool f16 = dqi.dtype == SDPA_F16;
+  hipError_t err = hipSuccess;
+  if (e.bwd_parts & 1)
+    err = timed_launch(SDPA_KERNEL_BWD_ROWS, st, [&] { return launch_bwd_rows(p, f16, st); });
+  if (err == hipSuccess && (e.bwd_parts & 2))
+    err = timed_launch(SDPA_KERNEL_BWD, st,
+                       [&] { return launch_bwd_main(p, causal, drop, f16, st); });
   return hip_status(err, "backward launch");
 }
 

@@ -375,3 +375,23 @@ def test_rows_whose_first_tiles_are_all_hidden(monkeypatch, shape, kind, causal)
     assert_out(host64(out), ref_out)
     assert_lse(lse.cpu().double().numpy(), ref_lse)
     assert_grads([(n, host64(a), r) for n, a, r in zip(("dq", "dk", "dv"), grads, ref_g)])
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,E,causal,p", [
+    (2, 3, 300, 300, 64, True, 0.1),
+    (1, 2, 130, 250, 128, False, 0.0),
+])
+def test_backward_in_two_parts_equals_one_call(B, H, Sq, Sk, E, causal, p):
+    say(f"backward as row pass, then main kernel: B{B} H{H} Sq{Sq} Sk{Sk} E{E}")
+    q, k, v, do = workloads.draw(B, H, Sq, Sk, E, 33, 1.0, "BHSE", device="cuda")
+    sdpa.sdpa_set_rng_state(9, 90)
+    out, lse, s, o = sdpa.sdpa_fwd(q, k, v, p, causal)
+    ref = sdpa.sdpa_bwd(do, q, k, v, out, lse, p, causal, s, o)
+    ws = torch.empty(sdpa.sdpa_bwd_workspace_size(B, H, Sq), dtype=torch.uint8, device="cuda")
+    got = tuple(torch.full_like(t, float("nan")) for t in (q, k, v))
+    sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, p, causal, s, o, None, *got, workspace=ws, bwd_parts=1)
+    assert all(torch.isnan(t.float()).all() for t in got)  # the row pass writes no gradient
+    sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, p, causal, s, o, None, *got, workspace=ws, bwd_parts=2)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)

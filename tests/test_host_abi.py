@@ -197,7 +197,15 @@ def test_forward_ext_rejects_bad_options(lib, ext, code, needle):
     assert bnd.sdpa_get_rng_state() == (31, 41)
 
 
+def _ext_parts(n):
+    e = _ext()
+    e.bwd_parts = n
+    return e
+
+
 @pytest.mark.parametrize("ext,code,needle", [
+    (_ext_parts(4), bnd.SDPA_ERR_INVALID, "bwd_parts"),
+    (_ext_parts(-1), bnd.SDPA_ERR_INVALID, "bwd_parts"),
     (_ext(head_offset=-3), bnd.SDPA_ERR_INVALID, "head_offset"),
     (_ext(head_offset=2, heads_total=3), bnd.SDPA_ERR_INVALID, "heads_total"),
     (_ext(rng_used=FAKE + 2), bnd.SDPA_ERR_UNSUPPORTED, "aligned"),
