@@ -104,6 +104,9 @@ typedef struct sdpa_tensor {
  *   q [B,H,Sq,E], k [B,H,Sk,E], v [B,H,Sk,E]  inputs, bf16.
  *   out [B,H,Sq,E]  output, bf16, any supported strides (usually q's).
  *   lse             output, fp32, contiguous [B,H,Sq] (B*H*Sq floats).
+ *                   The byte ranges of out and lse (and of keep_bits, see
+ *                   sdpa_ext) must not overlap one another or those of q, k, v
+ *                   and bias: SDPA_ERR_INVALID.  Inputs may share memory.
  *   seed, offset    host outputs: the Philox state this call used.  When
  *                   dropout_p > 0 the library state's offset then advances by
  *                   B*H*Sq*ceil(Sk/4); when dropout_p == 0 nothing advances
@@ -119,7 +122,10 @@ int sdpa_fwd(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* v,
  *   dout, q, k, v, out  bf16 inputs (out and lse as returned by sdpa_fwd).
  *   seed, offset        the values sdpa_fwd returned; ignored when dropout_p == 0.
  *   dq, dk, dv          bf16 outputs shaped like q, k, v (any supported strides);
- *                       they must not overlap the inputs.
+ *                       their byte ranges must not overlap those of any input
+ *                       (SDPA_ERR_INVALID).  They may be views of one packed
+ *                       buffer; that their elements are distinct is the
+ *                       caller's to ensure.
  *   workspace           device scratch owned by the caller, 256-byte aligned, at
  *                       least sdpa_bwd_workspace_size(B, H, Sq) bytes; it must not
  *                       overlap any tensor and may be reused once the call's work

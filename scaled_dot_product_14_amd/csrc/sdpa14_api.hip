@@ -92,7 +92,6 @@ bool same_shape(const Desc& a, const Desc& b) {
   return a.B == b.B && a.H == b.H && a.S == b.S && a.E == b.E;
 }
 
-// Kernels read rows of one (batch, head) slice through 32-bit buffer offsets.
 // Kernels address a (batch, head) slice with 32-bit byte offsets, including
 // rows past S that tiles and trailing ring loads reach (fewer than 256; those
 // read as zeros through the buffer range check).
@@ -114,6 +113,40 @@ int check_qkv(const Desc& q, const Desc& k, const Desc& v) {
   if (grid_f > kMaxGrid) return fail(SDPA_ERR_UNSUPPORTED, "problem too large for one launch");
   if (!slice_ok(q) || !slice_ok(k) || !slice_ok(v))
     return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice spans 2 GiB or more");
+  return SDPA_OK;
+}
+
+// Byte span [lo, hi) that a buffer's elements occupy.
+struct Span {
+  uintptr_t lo, hi;
+  const char* name;
+};
+
+Span tensor_span(const Desc& d, const char* name) {
+  const int64_t last = (d.B - 1) * d.st.b + (d.H - 1) * d.st.h + (d.S - 1) * d.st.s + d.E;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(d.ptr);
+  return Span{lo, lo + (uintptr_t)last * 2u, name};
+}
+
+Span raw_span(const void* p, size_t bytes, const char* name) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Span{lo, p == nullptr ? lo : lo + bytes, name};
+}
+
+// Every output span must be disjoint from every input span.  Outputs may share
+// a buffer with one another (views of one packed tensor) unless `pairwise`;
+// inputs may share anything.
+int check_disjoint(const Span* outs, int n_out, const Span* ins, int n_in, bool pairwise) {
+  for (int o = 0; o < n_out; ++o) {
+    if (outs[o].lo == outs[o].hi) continue;
+    for (int i = 0; i < n_in; ++i)
+      if (ins[i].lo != ins[i].hi && outs[o].lo < ins[i].hi && ins[i].lo < outs[o].hi)
+        return fail(SDPA_ERR_INVALID, "%s overlaps %s (outputs must not overlap inputs)",
+                    outs[o].name, ins[i].name);
+    for (int p = pairwise ? o + 1 : n_out; p < n_out; ++p)
+      if (outs[p].lo != outs[p].hi && outs[o].lo < outs[p].hi && outs[p].lo < outs[o].hi)
+        return fail(SDPA_ERR_INVALID, "%s overlaps %s", outs[o].name, outs[p].name);
+  }
   return SDPA_OK;
 }
 
@@ -159,6 +192,13 @@ struct Ext {
   uint32_t* keep_bits = nullptr;
   int bwd_parts = 3;  // bit 0: row pass, bit 1: main kernel
 };
+
+Span bias_span(const Ext& e, int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
+  if (e.bias == nullptr) return Span{0, 0, "bias"};
+  const int64_t last = (B - 1) * e.sbias.b + (H - 1) * e.sbias.h + (Sq - 1) * e.sbias.s + Sk;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(e.bias);
+  return Span{lo, lo + (uintptr_t)last * 2u, "bias"};
+}
 
 int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int dtype,
                Ext* e) {
@@ -363,6 +403,16 @@ int sdpa_fwd_ext(const sdpa_tensor* q, const sdpa_tensor* k, const sdpa_tensor* 
     return fail(SDPA_ERR_INVALID, "q, k, v and out must share one dtype");
   if ((rc = check_ext(ext, dq.B, dq.H, dq.S, dk.S, dq.dtype, true, &e))) return rc;
   const bool drop = dropout_p > 0.0;
+  {
+    const Span outs[3] = {tensor_span(dout, "out"),
+                          raw_span(lse, (size_t)(dq.B * dq.H * dq.S) * 4u, "lse"),
+                          raw_span(drop ? e.keep_bits : nullptr,
+                                   (size_t)(dq.B * dq.H * dq.S * keep_words(dk.S)) * 4u,
+                                   "keep_bits")};
+    const Span ins[4] = {tensor_span(dq, "q"), tensor_span(dk, "k"), tensor_span(dv, "v"),
+                         bias_span(e, dq.B, dq.H, dq.S, dk.S)};
+    if ((rc = check_disjoint(outs, 3, ins, 4, true))) return rc;
+  }
   const uint64_t advance = offset_advance(dq.B, e.heads_total, dq.S, dk.S);
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (forced_launch_failure("forward launch")) return SDPA_ERR_HIP;
@@ -502,6 +552,19 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
     if (d->dtype != dqi.dtype)
       return fail(SDPA_ERR_INVALID, "dout, q, k, v, out, dq, dk and dv must share one dtype");
   if ((rc = check_ext(ext, dqi.B, dqi.H, dqi.S, dki.S, dqi.dtype, false, &e))) return rc;
+  {
+    const int64_t rows = dqi.B * dqi.H * dqi.S;
+    const Span outs[4] = {tensor_span(dqo, "dq"), tensor_span(dko, "dk"), tensor_span(dvo, "dv"),
+                          raw_span(use_scratch ? nullptr : workspace,
+                                   bwd_workspace_bytes(dqi.B, dqi.H, dqi.S), "workspace")};
+    const Span ins[7] = {tensor_span(ddo, "dout"), tensor_span(dqi, "q"), tensor_span(dki, "k"),
+                         tensor_span(dvi, "v"), tensor_span(dout_i, "out"),
+                         raw_span(lse, (size_t)rows * 4u, "lse"),
+                         bias_span(e, dqi.B, dqi.H, dqi.S, dki.S)};
+    if ((rc = check_disjoint(outs, 4, ins, 7, false))) return rc;
+    // The workspace may not share memory with the gradients either.
+    if ((rc = check_disjoint(outs + 3, 1, outs, 3, false))) return rc;
+  }
 
   BwdParams p;
   p.q = dqi.ptr;

@@ -18,7 +18,10 @@ import scaled_dot_product_14_amd as sdpa
 from scaled_dot_product_14_amd import _binding as bnd
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+FAKE = 0x7F0000000000  # inputs: 16-byte aligned, never dereferenced
+FAKE_OUT = 0x7F1000000000  # outputs, LSE and workspace sit apart from the inputs
+FAKE_LSE = 0x7F2000000000
+FAKE_WS = 0x7F3000000000
 
 
 @pytest.fixture(scope="module")
@@ -54,11 +57,11 @@ def _t(B=1, H=2, S=128, E=64, layout="BHSE", data=FAKE, dtype=0, stride=None):
     return d
 
 
-def _fwd(lib, q=None, k=None, v=None, out=None, p=0.0, scale=math.nan, lse=FAKE):
+def _fwd(lib, q=None, k=None, v=None, out=None, p=0.0, scale=math.nan, lse=FAKE_LSE):
     q = q or _t()
     k = k or _t()
     v = v or _t()
-    out = out or _t()
+    out = out or _t(data=FAKE_OUT)
     s, o = ctypes.c_uint64(), ctypes.c_uint64()
     return lib.sdpa_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), p, 1, scale,
                         ctypes.byref(out), lse, ctypes.byref(s), ctypes.byref(o), None)
@@ -107,13 +110,17 @@ def test_forward_rejects_bad_arguments(lib, kw, code, needle):
 WS_BYTES = 1 << 20  # ample for the default shapes (B*H*Sq*8 = 2 KiB)
 
 
+_OUT_ADDR = {"dq": FAKE_OUT, "dk": FAKE_OUT + (1 << 32), "dv": FAKE_OUT + (2 << 32)}
+
+
 def _bwd(lib, **over):
-    t = {n: over.get(n) or _t() for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
+    t = {n: over.get(n) or _t(data=_OUT_ADDR.get(n, FAKE))
+         for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
     return lib.sdpa_bwd(*(ctypes.byref(t[n]) for n in ("dout", "q", "k", "v", "out")),
-                        over.get("lse", FAKE), over.get("p", 0.0), 1, 0, 0,
+                        over.get("lse", FAKE_LSE), over.get("p", 0.0), 1, 0, 0,
                         over.get("scale", math.nan),
                         *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")),
-                        over.get("ws", FAKE), over.get("ws_bytes", WS_BYTES), None)
+                        over.get("ws", FAKE_WS), over.get("ws_bytes", WS_BYTES), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -136,7 +143,7 @@ def test_backward_rejects_bad_arguments(lib, kw, code):
 
 @pytest.mark.parametrize("kw,needle", [
     (dict(ws=0), "NULL"),
-    (dict(ws=FAKE + 128), "aligned"),
+    (dict(ws=FAKE_WS + 128), "aligned"),
     (dict(ws_bytes=2047), "smaller"),
 ])
 def test_backward_checks_workspace(lib, kw, needle):
@@ -187,10 +194,10 @@ def _bias(size=(1, 2, 128, 128), stride=(0, 128 * 128, 128, 1), data=FAKE, dtype
 ])
 def test_forward_ext_rejects_bad_options(lib, ext, code, needle):
     bnd.sdpa_set_rng_state(31, 41)
-    q, k, v, out = _t(), _t(), _t(), _t()
+    q, k, v, out = _t(), _t(), _t(), _t(data=FAKE_OUT)
     s, o = ctypes.c_uint64(), ctypes.c_uint64()
     rc = lib.sdpa_fwd_ext(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0.1, 1, math.nan,
-                          ctypes.byref(out), FAKE, ctypes.byref(s), ctypes.byref(o),
+                          ctypes.byref(out), FAKE_LSE, ctypes.byref(s), ctypes.byref(o),
                           ctypes.byref(ext), None)
     assert rc == code, (rc, _err(lib))
     assert needle.lower() in _err(lib).lower()
@@ -211,11 +218,11 @@ def _ext_parts(n):
     (_ext(rng_used=FAKE + 2), bnd.SDPA_ERR_UNSUPPORTED, "aligned"),
 ])
 def test_backward_ext_rejects_bad_options(lib, ext, code, needle):
-    t = {n: _t() for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
+    t = {n: _t(data=_OUT_ADDR.get(n, FAKE)) for n in ("dout", "q", "k", "v", "out", "dq", "dk", "dv")}
     rc = lib.sdpa_bwd_ext(*(ctypes.byref(t[n]) for n in ("dout", "q", "k", "v", "out")),
-                          FAKE, 0.1, 1, 0, 0, math.nan,
+                          FAKE_LSE, 0.1, 1, 0, 0, math.nan,
                           *(ctypes.byref(t[n]) for n in ("dq", "dk", "dv")),
-                          FAKE, WS_BYTES, ctypes.byref(ext), None)
+                          FAKE_WS, WS_BYTES, ctypes.byref(ext), None)
     assert rc == code, (rc, _err(lib))
     assert needle.lower() in _err(lib).lower()
 
@@ -279,10 +286,10 @@ def test_keep_bits_alignment_checked(lib):
     bnd.sdpa_set_rng_state(61, 62)
     ext = _ext()
     ext.keep_bits = FAKE + 8
-    q, k, v, out = _t(), _t(), _t(), _t()
+    q, k, v, out = _t(), _t(), _t(), _t(data=FAKE_OUT)
     s, o = ctypes.c_uint64(), ctypes.c_uint64()
     rc = lib.sdpa_fwd_ext(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0.1, 1, math.nan,
-                          ctypes.byref(out), FAKE, ctypes.byref(s), ctypes.byref(o),
+                          ctypes.byref(out), FAKE_LSE, ctypes.byref(s), ctypes.byref(o),
                           ctypes.byref(ext), None)
     assert rc == bnd.SDPA_ERR_UNSUPPORTED and "keep_bits" in _err(lib)
     assert bnd.sdpa_get_rng_state() == (61, 62)
@@ -386,3 +393,40 @@ def test_describe_rejects_host_and_meta_tensors():
         bnd.describe(torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="GPU"):
         bnd.describe(torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="meta"))
+
+
+# ---- outputs must not overlap inputs -------------------------------------------
+
+
+def test_forward_output_overlapping_an_input_is_rejected(lib):
+    bnd.sdpa_set_rng_state(91, 92)
+    assert _fwd(lib, out=_t(data=FAKE)) == bnd.SDPA_ERR_INVALID
+    assert "out overlaps q" in _err(lib)
+    assert _fwd(lib, lse=FAKE + 4096) == bnd.SDPA_ERR_INVALID and "lse overlaps" in _err(lib)
+    # out and lse must not overlap each other either.
+    assert _fwd(lib, lse=FAKE_OUT + 64) == bnd.SDPA_ERR_INVALID and "overlaps lse" in _err(lib)
+    assert bnd.sdpa_get_rng_state() == (91, 92)
+
+
+def test_backward_gradients_overlapping_inputs_or_workspace_are_rejected(lib):
+    assert _bwd(lib, dq=_t(data=FAKE)) == bnd.SDPA_ERR_INVALID and "dq overlaps" in _err(lib)
+    assert _bwd(lib, dv=_t(data=FAKE_LSE)) == bnd.SDPA_ERR_INVALID and "dv overlaps lse" in _err(lib)
+    assert _bwd(lib, ws=FAKE) == bnd.SDPA_ERR_INVALID and "workspace overlaps" in _err(lib)
+    assert _bwd(lib, ws=FAKE_OUT + 1024) == bnd.SDPA_ERR_INVALID and "workspace overlaps dq" in _err(lib)
+
+
+def test_packed_views_pass_the_overlap_check(lib, monkeypatch):
+    # q, k, v as interleaved views of one packed [B, S, 3, H, E] buffer, and
+    # dq, dk, dv as views of another: shared memory within the inputs or within
+    # the gradients is fine.  With the launch hook set, a call that passes
+    # validation returns SDPA_ERR_HIP.
+    monkeypatch.setenv("SDPA14_FAIL_LAUNCH", "1")
+    B, H, S, E = 1, 2, 128, 64
+    st = (S * 3 * H * E, E, 3 * H * E, 1)
+    qkv = [_t(B, H, S, E, data=FAKE + i * H * E * 2, stride=st) for i in range(3)]
+    dqkv = [_t(B, H, S, E, data=FAKE_OUT + i * H * E * 2, stride=st) for i in range(3)]
+    out = _t(B, H, S, E, data=FAKE_OUT + (1 << 33))
+    rc = _fwd(lib, q=qkv[0], k=qkv[1], v=qkv[2], out=out)
+    assert rc == bnd.SDPA_ERR_HIP, _err(lib)
+    rc = _bwd(lib, q=qkv[0], k=qkv[1], v=qkv[2], out=out, dq=dqkv[0], dk=dqkv[1], dv=dqkv[2])
+    assert rc == bnd.SDPA_ERR_HIP, _err(lib)
