@@ -36,6 +36,11 @@ Steps, per head, with s the scale:
 7. O = (P * M) V.
 8. Backward: dPd = dO V^T; dP = dPd * M; D_i = sum_j P_ij dP_ij;
    dS = P * (dP - D); dQ = s dS K; dK = s dS^T Q; dV = (P * M)^T dO.
+9. Bias gradient (the forum thread's opening question wants the relative
+   position term trained through SDPA): S = s Q K^T + bias, so the gradient
+   with respect to the bias as head (b, h) sees it is dS itself, zero where
+   the mask hides a score.  Where the bias broadcasts over a dimension,
+   summing dS over it is the broadcast's own backward, outside attention.
 
 D is formed as sum_j P dP, which equals rowsum(dO * O) in exact arithmetic.
 """
@@ -99,9 +104,11 @@ def head_forward(qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray, bias
     return out, lse, P
 
 
-def head_backward(dOh, qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray, bias_h=None):
-    """Steps 2-8 on one head.  Returns (dQ, dK, dV, D).  The bias enters through
-    P only: S = s Q K^T + bias, so dQ and dK keep their form."""
+def head_backward(dOh, qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray, bias_h=None,
+                  want_ds: bool = False):
+    """Steps 2-8 on one head.  Returns (dQ, dK, dV, D), and dS last with
+    ``want_ds`` (step 9: the bias gradient).  The bias enters through P only:
+    S = s Q K^T + bias, so dQ and dK keep their form."""
     _, _, P = head_forward(qh, kh, vh, s, valid, mult, bias_h)
     dPd = dOh @ vh.T
     dP = dPd * mult
@@ -110,6 +117,8 @@ def head_backward(dOh, qh, kh, vh, s: float, valid: np.ndarray, mult: np.ndarray
     dq = s * (dS @ kh)
     dk = s * (dS.T @ qh)
     dv = (P * mult).T @ dOh
+    if want_ds:
+        return dq, dk, dv, D, dS
     return dq, dk, dv, D
 
 
@@ -169,11 +178,13 @@ def fwd_rows(q, k, v, b: int, h: int, rows, dropout_p: float = 0.0, is_causal: b
 
 
 def bwd(dout, q, k, v, dropout_p: float = 0.0, is_causal: bool = False, seed: int = 0,
-        offset: int = 0, scale=None, heads=None, bias=None):
+        offset: int = 0, scale=None, heads=None, bias=None, want_dbias: bool = False):
     """Backward on logical [B, H, S, E] inputs: ``(dq, dk, dv)`` in float64.
 
     Computed from (dO, Q, K, V, p, seed, offset, causal, scale) alone; the
-    forward's outputs are recomputed, never taken from the caller.
+    forward's outputs are recomputed, never taken from the caller.  With
+    ``want_dbias`` a fourth array follows: the bias gradient of step 9, shape
+    [B, H, Sq, Sk] (NaN for heads not computed).
     """
     dout, q, k, v = _as64(dout), _as64(q), _as64(k), _as64(v)
     B, H, Sq, E = q.shape
@@ -184,9 +195,14 @@ def bwd(dout, q, k, v, dropout_p: float = 0.0, is_causal: bool = False, seed: in
     dv = np.full(v.shape, np.nan)
     valid = valid_mask(Sq, Sk, is_causal)
     bias = _bias64(bias, B, H, Sq, Sk)
+    dbias = np.full((B, H, Sq, Sk), np.nan) if want_dbias else None
     for b, h in _heads(B, H, heads):
         mult = dropout_multiplier(dropout_p, seed, offset, B, H, Sq, Sk, b, h)
-        dq[b, h], dk[b, h], dv[b, h], _ = head_backward(
-            dout[b, h], q[b, h], k[b, h], v[b, h], s, valid, mult,
-            None if bias is None else bias[b, h])
+        r = head_backward(dout[b, h], q[b, h], k[b, h], v[b, h], s, valid, mult,
+                          None if bias is None else bias[b, h], want_ds=want_dbias)
+        dq[b, h], dk[b, h], dv[b, h] = r[:3]
+        if want_dbias:
+            dbias[b, h] = r[4]
+    if want_dbias:
+        return dq, dk, dv, dbias
     return dq, dk, dv

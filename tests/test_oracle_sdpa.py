@@ -295,6 +295,77 @@ def test_bias_finite_differences_with_dropout():
         assert err <= 1e-6 or np.abs(fd - g).max() < 1e-8, (i, err)
 
 
+# ---- bias gradient (step 9 of the oracle) ----------------------------------------
+
+
+@pytest.mark.parametrize("Sq,Sk", [(3, 4), (5, 7), (4, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p", [0.0, 0.3])
+def test_dbias_finite_differences(Sq, Sk, causal, p):
+    # Central differences of sum(dO * O) in every bias entry of a full
+    # [B, H, Sq, Sk] bias; entries a row cannot see must get exactly zero.
+    B, H, E = 1, 2, 4
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=60 + Sq * 5 + Sk)
+    bias = _rand((B, H, Sq, Sk), 61 + Sq, 1.5)
+    seed, off = 99, 11
+
+    def loss(bb):
+        out, _ = sdpa_ref.fwd(q, k, v, p, causal, None, seed, off, bias=bb)
+        return float((do * out).sum())
+
+    *_, db = sdpa_ref.bwd(do, q, k, v, p, causal, seed, off, bias=bias, want_dbias=True)
+    step = 1e-6
+    fd = np.zeros_like(bias)
+    for idx in np.ndindex(bias.shape):
+        bp, bm = bias.copy(), bias.copy()
+        bp[idx] += step
+        bm[idx] -= step
+        fd[idx] = (loss(bp) - loss(bm)) / (2 * step)
+    err = np.linalg.norm(fd - db) / max(np.linalg.norm(db), 1e-30)
+    assert err <= 1e-6 or np.abs(fd - db).max() < 1e-8, err
+    hidden = ~sdpa_ref.valid_mask(Sq, Sk, causal)
+    assert (db[:, :, hidden] == 0).all()
+
+
+@pytest.mark.parametrize("shape,bshape,causal", [
+    ((1, 2, 48, 64, 32), (1, 2, 48, 64), False),
+    ((2, 2, 40, 40, 16), (1, 2, 40, 40), True),
+    ((2, 3, 32, 56, 16), (32, 56), True),
+])
+def test_dbias_against_torch_attn_mask_grad(shape, bshape, causal):
+    # PyTorch's float attn_mask with requires_grad: its gradient is the bias
+    # gradient summed over the dimensions the mask broadcasts.
+    B, H, Sq, Sk, E = shape
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=62)
+    bias = _rand(bshape, 63, 2.0)
+    s = 1 / math.sqrt(E)
+    *_, db = sdpa_ref.bwd(do, q, k, v, 0.0, causal, bias=bias, want_dbias=True)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    tb = torch.tensor(bias, dtype=torch.float64, requires_grad=True)
+    mask = tb.expand(B, H, Sq, Sk)
+    if causal:
+        tri = torch.ones(Sq, Sk, dtype=torch.bool).tril()
+        mask = mask.masked_fill(~tri, -math.inf)
+    t_out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=s)
+    t_out.backward(torch.tensor(do, dtype=torch.float64))
+    summed = db.reshape((B, H, Sq, Sk))
+    lead = len(summed.shape) - len(bshape)
+    summed = summed.sum(axis=tuple(range(lead)))
+    for ax, n in enumerate(bshape):
+        if n == 1:
+            summed = summed.sum(axis=ax, keepdims=True)
+    assert np.allclose(summed, tb.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_dbias_rows_sum_to_zero_with_dropout():
+    # sum_j dS_ij = sum_j P_ij dP_ij - D_i sum_j P_ij = D_i - D_i = 0 on every row.
+    B, H, Sq, Sk, E = 2, 2, 37, 53, 16
+    q, k, v, do = _case(B, H, Sq, Sk, E, seed=64)
+    bias = _rand((B, H, Sq, Sk), 65, 1.0)
+    *_, db = sdpa_ref.bwd(do, q, k, v, 0.25, True, 3, 8, bias=bias, want_dbias=True)
+    assert np.abs(db.sum(axis=3)).max() < 1e-12 * np.abs(db).max() * Sk
+
+
 # ---- non-finite inputs --------------------------------------------------------
 # The definition fixes what a NaN or an infinity does: only the outputs whose
 # defining sums contain it are NaN.  A query row enters only its own row of S;
