@@ -20,7 +20,8 @@ Prints ONE JSON line:
 
 Options: --steps K --warmup W --gpus N (N must be 1), --no-cpu-baseline,
 --workload NAME, --shape B,H,Sq,Sk,E,causal[,p], --bias {none,qk,bhqk} (an additive bias through the
-extended calls), --copy-bytes N (time a plain device copy of N bytes instead, for calibrating
+extended calls), --dbias (with a bias: the backward also writes the [B, H, Sq, Sk] bias
+gradient), --copy-bytes N (time a plain device copy of N bytes instead, for calibrating
 hardware byte counters).
 """
 
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--bias", choices=("none", "qk", "bhqk"), default="none",
                     help="add an additive bf16 bias: [Sq, Sk] broadcast over batch and heads, "
                          "or a full [B, H, Sq, Sk] (drawn N(0, 4)); timed through the extended calls")
+    ap.add_argument("--dbias", action="store_true",
+                    help="with --bias: the backward also writes the full [B, H, Sq, Sk] bias gradient")
     ap.add_argument("--shape", default="",
                     help="B,H,Sq,Sk,E,causal[,p] instead of a named workload (exploration)")
     return ap.parse_args()
@@ -222,6 +225,12 @@ def main():
         gb = torch.Generator("cpu").manual_seed(8)
         bshape = (w.Sq, w.Sk) if args.bias == "qk" else (w.B, w.H, w.Sq, w.Sk)
         bias = (torch.randn(bshape, generator=gb) * 2.0).to(torch.bfloat16).to("cuda")
+    dbias = None
+    if args.dbias:
+        if bias is None:
+            raise SystemExit("--dbias needs --bias")
+        dbias = torch.empty((w.B, w.H, w.Sq, -(-w.Sk // 8) * 8), dtype=torch.bfloat16,
+                            device="cuda")[..., :w.Sk]
 
     keep = None
     if args.keep_bits:
@@ -244,7 +253,7 @@ def main():
         else:
             sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, w.dropout_p, w.causal, s, o, None, dq=dq,
                               dk=dk, dv=dv, workspace=ws, bias=bias, keep_bits=keep,
-                              bwd_parts=parts)
+                              bwd_parts=parts, dbias=dbias)
 
     def step():
         fwd()
@@ -388,7 +397,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "E": w.E,
                    "layout": w.layout, "causal": w.causal, "dropout_p": w.dropout_p,
-                   "bias": args.bias, "keep_bits": bool(args.keep_bits),
+                   "bias": args.bias, "dbias": bool(args.dbias), "keep_bits": bool(args.keep_bits),
                    "cache": "warm (same buffers every step)"},
         "timing": "graph replay of the captured step (eager_ms_per_step: the same step "
                   "issued from Python each time)",

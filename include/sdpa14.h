@@ -180,7 +180,7 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       so the rest of the granule holding a slice's last element is read
  *       (and ignored).  -inf entries hide a key; every row
  *       must keep at least one visible key with a finite score.  Forward and
- *       backward must be given the same bias; its gradient is not computed.
+ *       backward must be given the same bias; dbias below asks for its gradient.
  *   keep_bits  (NULL for none; used only when dropout_p > 0)
  *       Device buffer of sdpa_keep_bits_size(B, H, Sq, Sk) bytes, 16-byte
  *       aligned.  The forward writes the dropout keep bits it draws there (bit
@@ -196,6 +196,18 @@ int sdpa_bwd(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
  *       same dout, out, lse and scale filled earlier in stream order), 3 or 0
  *       both.  Lets a caller overlap the row pass with other work and time the
  *       two kernels apart; the arguments are validated in full either way.
+ *   dbias  (backward only, NULL for none; the forward ignores it)
+ *       The bias gradient, for a relative-position term trained through SDPA
+ *       (forum thread "Scaled_dot_product_attention", opening question): with
+ *       S = scale * q_i . k_j + bias[b, h, i, j], dbias[b, h, i, j] = dL/dS_ij
+ *       = P_ij * (dP_ij - D_i), the gradient with respect to the bias as head
+ *       (b, h) sees it, and exactly 0 where the causal mask hides the score.
+ *       Logical shape [B, H, Sq, Sk], written in full, in q's dtype; key
+ *       stride 1, other strides positive multiples of 8 elements with no two
+ *       elements sharing memory, data 16-byte aligned, its memory disjoint
+ *       from every other argument.  Where the bias broadcasts over a dimension
+ *       (stride 0), the caller sums dbias over it: that is the broadcast's own
+ *       backward.  Needs bias; written by the main kernel (bwd_parts 2 or 3).
  */
 typedef struct sdpa_ext {
   int64_t head_offset;
@@ -205,6 +217,7 @@ typedef struct sdpa_ext {
   const sdpa_tensor* bias;
   uint32_t* keep_bits;
   int32_t bwd_parts;
+  const sdpa_tensor* dbias;
 } sdpa_ext;
 
 /* sdpa_fwd / sdpa_bwd with options; sdpa_fwd and sdpa_bwd are these with ext == NULL.

@@ -56,6 +56,7 @@ class SdpaExt(ctypes.Structure):
         ("bias", ctypes.POINTER(SdpaTensor)),
         ("keep_bits", ctypes.c_void_p),
         ("bwd_parts", ctypes.c_int32),
+        ("dbias", ctypes.POINTER(SdpaTensor)),
     ]
 
 
@@ -261,7 +262,7 @@ def sdpa_keep_bits_size(B: int, H: int, Sq: int, Sk: int) -> int:
 
 
 def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None, keep_bits=None,
-         device=None, bwd_parts=0):
+         device=None, bwd_parts=0, dbias=None):
     """The options block and the objects it points into (keep both alive for the call)."""
     e = SdpaExt()
     e.bwd_parts = int(bwd_parts)
@@ -282,6 +283,10 @@ def _ext(head_offset, heads_total, rng_state, rng_used, bias=None, shape=None, k
         desc = describe(full, device, "bias")
         e.bias = ctypes.pointer(desc)
         keep = (full, desc)
+    if dbias is not None:
+        ddesc = describe(dbias, device, "dbias")
+        e.dbias = ctypes.pointer(ddesc)
+        keep = (keep, ddesc)
     return e, keep
 
 
@@ -331,13 +336,15 @@ def sdpa_fwd_ext(q, k, v, dropout_p: float = 0.0, is_causal: bool = False, scale
 def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int = 0,
                  offset: int = 0, scale=None, dq=None, dk=None, dv=None, workspace=None, *,
                  head_offset: int = 0, heads_total: int = 0, rng_used=None, bias=None,
-                 keep_bits=None, bwd_parts: int = 0):
+                 keep_bits=None, bwd_parts: int = 0, dbias=None):
     """Backward with options (see ``sdpa_fwd_ext``): returns ``(dq, dk, dv)``.
 
     With ``rng_used`` the kernels read (seed, offset) from that device tensor
     and ``seed`` / ``offset`` are ignored.  ``bwd_parts`` picks the kernels to
     enqueue: 1 the row pass (fills ``workspace``), 2 the main kernel (reads a
-    workspace a row pass filled), 0 or 3 both.
+    workspace a row pass filled), 0 or 3 both.  ``dbias`` (a [B, H, Sq, Sk]
+    tensor of q's dtype, needs ``bias``) receives the bias gradient of every
+    head; sum it over the dimensions the bias broadcasts.
     """
     lib = load_library()
     _on_device(q, None, "q")
@@ -354,7 +361,7 @@ def sdpa_bwd_ext(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, see
         (dout, q, k, v, out, dq, dk, dv), ("dout", "q", "k", "v", "out", "dq", "dk", "dv"))]
     ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
                       (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device,
-                      bwd_parts)
+                      bwd_parts, dbias)
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd_ext(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                               float(dropout_p), int(bool(is_causal)), int(seed), int(offset),
@@ -405,7 +412,7 @@ def sdpa_bwd_noalloc_max_rows() -> int:
 
 def sdpa_bwd_noalloc(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool, seed: int,
                      offset: int, scale, dq, dk, dv, *, head_offset: int = 0,
-                     heads_total: int = 0, rng_used=None, bias=None, keep_bits=None):
+                     heads_total: int = 0, rng_used=None, bias=None, keep_bits=None, dbias=None):
     """Backward that allocates nothing: the caller passes dq, dk, dv and the
     library uses its own device-resident scratch for the row pass.  Returns
     ``(dq, dk, dv)``.  Calls that overlap on one device race (shared scratch)."""
@@ -415,7 +422,8 @@ def sdpa_bwd_noalloc(dout, q, k, v, out, lse, dropout_p: float, is_causal: bool,
     descs = [describe(t, q.device, n) for t, n in zip(
         (dout, q, k, v, out, dq, dk, dv), ("dout", "q", "k", "v", "out", "dq", "dk", "dv"))]
     ext, _keep = _ext(head_offset, heads_total, None, rng_used, bias,
-                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device)
+                      (q.shape[0], q.shape[1], q.shape[2], k.shape[2]), keep_bits, q.device,
+                      0, dbias)
     with torch.cuda.device(q.device):
         rc = lib.sdpa_bwd_noalloc(*(ctypes.byref(d) for d in descs[:5]), lse.data_ptr(),
                                   float(dropout_p), int(bool(is_causal)), int(seed), int(offset),

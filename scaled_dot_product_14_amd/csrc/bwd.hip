@@ -24,6 +24,10 @@
 //                 keeps its rows' Q and dO fragments, D and LSE in registers.
 //                 Per key tile: S^T = K Q^T, dP^T = V dO^T (lane = row), dS'^T
 //                 as above, dQ^T += K^T dS'^T with K^T read transposed.
+//                 With a bias gradient asked for, the role also stores
+//                 dS = Ps * (dP - D) / scale for its block: it meets every
+//                 (row, key) of the block exactly once, and writes zeros for
+//                 the rows a causal mask hides from all of the block's keys.
 //               The tiles a workgroup streams (Q and dO, or K and V) go straight
 //               from memory to LDS (buffer loads with the LDS destination), into
 //               a ring of three stages filled two iterations ahead, so neither
@@ -54,6 +58,12 @@ template <typename P>
 __device__ __forceinline__ uint32_t bias_bytes(const P& p) {
   const int64_t b = ((int64_t)(p.Sq - 1) * p.sbias.s + p.Sk) * 2;
   return (uint32_t)((b + 7) & ~int64_t(7));
+}
+
+// Bytes of one (batch, head) slice of the bias gradient.
+template <typename P>
+__device__ __forceinline__ uint32_t dbias_bytes(const P& p) {
+  return (uint32_t)(((int64_t)(p.Sq - 1) * p.sdbias.s + p.Sk) * 2);
 }
 
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -181,7 +191,7 @@ __device__ __forceinline__ void exchange_finish(const f32x16 (&acc)[E / 32], flo
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP, bool DBIAS>
 __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
                                           unsigned char* lds) {
   using C = BwdCfg<E, BIAS, KEEP>;
@@ -237,6 +247,18 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     br = make_rsrc(p.bias + b * p.sbias.b + h * p.sbias.h, bias_bytes(p));
 #pragma unroll
     for (int k = 0; k < 2; ++k) obias[k] = dma_src_offset<64>(k, tid, p.sbias.s) + (uint32_t)kb0 * 2u;
+  }
+  // Bias gradient: element (row, key) goes to byte offset 2 * (row * sdb + key)
+  // of the head's slice.  A lane's register r holds row q0 + 8*(r/4) + 4*g +
+  // r%4 of its key: the lane part (4*g rows, the key) is a vector offset, the
+  // rest a wave-uniform scalar offset per store.
+  __amdgpu_buffer_rsrc_t rdb = make_rsrc(p.q, 0u);
+  uint32_t odb = 0u, sdb2 = 0u;
+  const float inv_scale = 1.f / p.scale;
+  if (DBIAS) {
+    rdb = make_rsrc(p.dbias + b * p.sdbias.b + h * p.sdbias.h, dbias_bytes(p));
+    sdb2 = (uint32_t)p.sdbias.s * 2u;
+    odb = (uint32_t)(4 * g) * sdb2 + (uint32_t)key * 2u;
   }
 
   // Stage it % 3 of the ring holds query tiles t0 + 2*it and t0 + 2*it + 1.
@@ -341,7 +363,19 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
     // Every step issues the loads of stage it+2, also past the last stage (those
     // rows lie past Sq and read as zeros into a stage nobody reads again), so
     // the issue points need no branch and every barrier waits the same count.
-    if (!active) issue(it + 2);
+    if (!active) {
+      issue(it + 2);
+      // A causal tile whose rows all precede this sub-block's keys: its bias
+      // gradient is zero.  Lanes g = 0, 1 take rows q0 .. q0+15, q0+16 .. q0+31.
+      if (DBIAS && q0 < p.Sq && key < p.Sk) {
+#pragma unroll 4
+        for (int r = 0; r < 16; ++r)
+          if (q0 + 16 * g + r < p.Sq)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rdb,
+                                                  (uint32_t)(16 * g) * sdb2 + (uint32_t)key * 2u,
+                                                  (uint32_t)(q0 + r) * sdb2, 0);
+      }
+    }
     if (active) {
       const unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
       const unsigned char* tq = st + ST_Q + qs * TILE_B;
@@ -415,6 +449,17 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
             }
             pb[r >> 3][r & 7] = to16<F16>(pd);
             dsb[r >> 3][r & 7] = to16<F16>(ps * dp);
+            if (DBIAS) {
+              // ps carries the scale: dS = ps * (dP - D) / scale.  Causally
+              // hidden elements store ps = 0; only rows past Sq and keys past
+              // Sk (ragged tiles) are skipped.
+              bool in = true;
+              if (MASK) in = (q0 + 8 * cg + 4 * g + u < p.Sq) & (key < p.Sk);
+              if (in)
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    __builtin_bit_cast(uint16_t, to16<F16>(ps * dp * inv_scale)), rdb, odb,
+                    (uint32_t)(q0 + 8 * cg + u) * sdb2, 0);
+            }
             if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
           }
         }
@@ -451,6 +496,25 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
   exchange_finish<E, F16>(dva, 1.f / p.scale, dvp, p.sdv.s, kbs, p.Sk, p.E, red, partner + 0, upper,
                           lane);
   exchange_finish<E, F16>(dka, 1.f, dkp, p.sdk.s, kbs, p.Sk, p.E, red, partner + 1, upper, lane);
+
+  // Rows before the first tile this block visits (causal: every key of the
+  // block is hidden from them) get a zero bias gradient: 8 lanes per row, 16
+  // bytes (8 keys) each, the rows dealt over the workgroup.
+  if (DBIAS && CAUSAL) {
+    const int rows = min(t0 * 32, p.Sq);
+    const int k8 = kb0 + 8 * (tid & 7);
+    if (k8 < p.Sk) {
+      for (int r = tid >> 3; r < rows; r += 32) {
+        const uint32_t off = (uint32_t)r * sdb2 + (uint32_t)k8 * 2u;
+        if (k8 + 8 <= p.Sk) {
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, rdb, off, 0u, 0);
+        } else {
+          for (int j = 0; j < p.Sk - k8; ++j)
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)0, rdb, off + 2u * (uint32_t)j, 0u, 0);
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -718,7 +782,7 @@ struct BwdOrder {
 // Workgroup order: per head, blocks in BwdOrder order (or, past kMaxOrder
 // blocks, dK/dV and dQ alternating, heaviest causal blocks first); all blocks
 // of a head sit on one XCD when the head count allows.
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP, bool DBIAS>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb, BwdOrder ord,
                                                   int use_order) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E, BIAS, KEEP>::LDS_B];
@@ -750,7 +814,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb,
     }
   }
   if (dkdv)
-    role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16, KEEP>(p, bh, rank, lds);
+    role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16, KEEP, DBIAS>(p, bh, rank, lds);
   else
     role_dq<E, CAUSAL, DROPOUT, BIAS, F16, KEEP>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
@@ -828,10 +892,20 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStrea
                      [](const Item& a, const Item& b) { return a.cost > b.cost; });
     for (size_t i = 0; i < items.size(); ++i) ord.item[i] = (uint16_t)items[i].key;
   }
-  auto go2 = [&](auto c, auto d, auto bias, auto keep) {
+  auto go3 = [&](auto c, auto d, auto bias, auto keep, auto db) {
     hipLaunchKernelGGL((bwd_kernel<E, decltype(c)::value, decltype(d)::value,
-                                   decltype(bias)::value, F16, decltype(keep)::value>),
+                                   decltype(bias)::value, F16, decltype(keep)::value,
+                                   decltype(db)::value>),
                        grid, dim3(256), 0, stream, p, nkb, nqb, ord, use_order);
+  };
+  auto go2 = [&](auto c, auto d, auto bias, auto keep) {
+    if constexpr (decltype(bias)::value) {
+      if (p.dbias != nullptr) {
+        go3(c, d, bias, keep, Flag<true>{});
+        return;
+      }
+    }
+    go3(c, d, bias, keep, Flag<false>{});
   };
   auto go = [&](auto c, auto d, auto bias) {
     if constexpr (decltype(d)::value) {

@@ -53,6 +53,8 @@ struct BwdParams {
   Strides sbias;
   const uint32_t* keep;  // keep bits written by the forward, or null: regenerate
   int keep_w;
+  uint16_t* dbias;       // bias gradient [B, H, Sq, Sk] (needs bias), or null: not computed
+  Strides sdbias;
 };
 
 struct MaskParams {

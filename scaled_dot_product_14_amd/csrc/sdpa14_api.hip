@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -191,7 +192,16 @@ struct Ext {
   Strides sbias{0, 0, 0};
   uint32_t* keep_bits = nullptr;
   int bwd_parts = 3;  // bit 0: row pass, bit 1: main kernel
+  uint16_t* dbias = nullptr;  // backward only
+  Strides sdbias{0, 0, 0};
 };
+
+Span dbias_span(const Ext& e, int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
+  if (e.dbias == nullptr) return Span{0, 0, "dbias"};
+  const int64_t last = (B - 1) * e.sdbias.b + (H - 1) * e.sdbias.h + (Sq - 1) * e.sdbias.s + Sk;
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(e.dbias);
+  return Span{lo, lo + (uintptr_t)last * 2u, "dbias"};
+}
 
 Span bias_span(const Ext& e, int64_t B, int64_t H, int64_t Sq, int64_t Sk) {
   if (e.bias == nullptr) return Span{0, 0, "bias"};
@@ -217,6 +227,39 @@ int check_bias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t S
     return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice of the bias spans 2 GiB or more");
   e->bias = static_cast<const uint16_t*>(t->data);
   e->sbias = Strides{t->stride[0], t->stride[1], t->stride[2]};
+  return SDPA_OK;
+}
+
+// The bias gradient has one element per (b, h, i, j), written once each, so no
+// two of its elements may share memory.
+int check_dbias(const sdpa_tensor* t, int64_t B, int64_t H, int64_t Sq, int64_t Sk, int dtype,
+                Ext* e) {
+  if (t->data == nullptr) return fail(SDPA_ERR_INVALID, "dbias data is NULL");
+  if (t->dtype != dtype) return fail(SDPA_ERR_UNSUPPORTED, "dbias dtype must be the dtype of q");
+  if (t->size[0] != B || t->size[1] != H || t->size[2] != Sq || t->size[3] != Sk)
+    return fail(SDPA_ERR_INVALID, "dbias must have logical shape [B, H, Sq, Sk]");
+  if (t->stride[3] != 1) return fail(SDPA_ERR_UNSUPPORTED, "dbias key stride must be 1");
+  for (int i = 0; i < 3; ++i)
+    if (t->stride[i] < 1 || t->stride[i] % 8 != 0)
+      return fail(SDPA_ERR_UNSUPPORTED, "dbias strides must be positive multiples of 8 elements");
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "dbias data is not 16-byte aligned");
+  // Taken in order of stride, each dimension must step past everything the
+  // dimensions below it span.
+  struct Dim {
+    int64_t n, s;
+  } d[3] = {{B, t->stride[0]}, {H, t->stride[1]}, {Sq, t->stride[2]}};
+  std::sort(d, d + 3, [](const Dim& a, const Dim& b) { return a.s < b.s; });
+  int64_t extent = Sk;
+  for (const Dim& x : d) {
+    if (x.n == 1) continue;
+    if (x.s < extent) return fail(SDPA_ERR_INVALID, "dbias elements overlap (strides too small)");
+    extent = x.s * (x.n - 1) + extent;
+  }
+  if (((Sq - 1) * t->stride[2] + Sk) * 2 >= (int64_t(1) << 31))
+    return fail(SDPA_ERR_UNSUPPORTED, "a (batch, head) slice of dbias spans 2 GiB or more");
+  e->dbias = static_cast<uint16_t*>(t->data);
+  e->sdbias = Strides{t->stride[0], t->stride[1], t->stride[2]};
   return SDPA_OK;
 }
 
@@ -251,6 +294,12 @@ int check_ext(const sdpa_ext* ext, int64_t B, int64_t H, int64_t Sq, int64_t Sk,
       if (ext->bwd_parts < 0 || ext->bwd_parts > 3)
         return fail(SDPA_ERR_INVALID, "bwd_parts = %d not in 0..3", ext->bwd_parts);
       e.bwd_parts = ext->bwd_parts == 0 ? 3 : ext->bwd_parts;
+      if (ext->dbias != nullptr) {
+        if (ext->bias == nullptr)
+          return fail(SDPA_ERR_INVALID, "dbias needs a bias (the gradient is taken with respect to it)");
+        const int rc = check_dbias(ext->dbias, B, H, Sq, Sk, dtype, &e);
+        if (rc) return rc;
+      }
     }
     if (reinterpret_cast<uintptr_t>(e.keep_bits) % 16 != 0)
       return fail(SDPA_ERR_UNSUPPORTED, "keep_bits is not 16-byte aligned");
@@ -564,6 +613,10 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
     if ((rc = check_disjoint(outs, 4, ins, 7, false))) return rc;
     // The workspace may not share memory with the gradients either.
     if ((rc = check_disjoint(outs + 3, 1, outs, 3, false))) return rc;
+    // Nor the bias gradient with any other argument.
+    const Span db = dbias_span(e, dqi.B, dqi.H, dqi.S, dki.S);
+    if ((rc = check_disjoint(&db, 1, ins, 7, false))) return rc;
+    if ((rc = check_disjoint(&db, 1, outs, 4, false))) return rc;
   }
 
   BwdParams p;
@@ -597,6 +650,8 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
   p.sbias = e.sbias;
   p.keep = dropout_p > 0.0 ? e.keep_bits : nullptr;
   p.keep_w = keep_words(dki.S);
+  p.dbias = e.dbias;
+  p.sdbias = e.sdbias;
   const bool causal = is_causal != 0, drop = dropout_p > 0.0;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (forced_launch_failure("backward launch")) return SDPA_ERR_HIP;

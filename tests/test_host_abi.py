@@ -227,6 +227,55 @@ def test_backward_ext_rejects_bad_options(lib, ext, code, needle):
     assert needle.lower() in _err(lib).lower()
 
 
+FAKE_DB = 0x7F4000000000
+
+
+def _ext_db(bias=True, **kw):
+    e = _ext(bias=_bias() if bias else None)
+    d = _bias(**{"data": FAKE_DB, "stride": (2 * 128 * 128, 128 * 128, 128, 1), **kw})
+    _BIAS_KEEP.append(d)
+    e.dbias = ctypes.pointer(d)
+    return e
+
+
+@pytest.mark.parametrize("ext,code,needle", [
+    (_ext_db(bias=False), bnd.SDPA_ERR_INVALID, "needs a bias"),
+    (_ext_db(data=0), bnd.SDPA_ERR_INVALID, "dbias data"),
+    (_ext_db(dtype=1), bnd.SDPA_ERR_UNSUPPORTED, "dbias dtype"),
+    (_ext_db(size=(1, 2, 128, 64)), bnd.SDPA_ERR_INVALID, "shape"),
+    (_ext_db(stride=(2 * 128 * 128, 128 * 128, 1, 128)), bnd.SDPA_ERR_UNSUPPORTED, "key stride"),
+    (_ext_db(stride=(2 * 128 * 128, 0, 128, 1)), bnd.SDPA_ERR_UNSUPPORTED, "positive"),
+    (_ext_db(stride=(2 * 128 * 128, 128 * 128, 132, 1)), bnd.SDPA_ERR_UNSUPPORTED, "multiples of 8"),
+    (_ext_db(data=FAKE_DB + 8), bnd.SDPA_ERR_UNSUPPORTED, "16-byte"),
+    # Rows 64 elements apart with 128 keys: elements of neighbouring rows coincide.
+    (_ext_db(stride=(2 * 128 * 128, 128 * 128, 64, 1)), bnd.SDPA_ERR_INVALID, "overlap"),
+    # Heads 64 rows apart with 128 rows per head.
+    (_ext_db(stride=(2 * 128 * 128, 64 * 128, 128, 1)), bnd.SDPA_ERR_INVALID, "overlap"),
+    (_ext_db(stride=(2 * 128 * 128, 128 * 128, 1 << 24, 1)), bnd.SDPA_ERR_UNSUPPORTED, "2 GiB"),
+    (_ext_db(data=FAKE), bnd.SDPA_ERR_INVALID, "dbias overlaps"),
+    (_ext_db(data=FAKE_OUT), bnd.SDPA_ERR_INVALID, "dbias overlaps dq"),
+    (_ext_db(data=FAKE_WS), bnd.SDPA_ERR_INVALID, "dbias overlaps workspace"),
+])
+def test_backward_rejects_bad_bias_gradient(lib, ext, code, needle):
+    test_backward_ext_rejects_bad_options(lib, ext, code, needle)
+
+
+def test_bias_gradient_layouts_pass_validation(lib, monkeypatch):
+    # Accepted layouts reach the launch (the hook then returns SDPA_ERR_HIP):
+    # contiguous, a batch stride that B = 1 never uses, padded rows.  The
+    # forward ignores dbias.
+    monkeypatch.setenv("SDPA14_FAIL_LAUNCH", "1")
+    for st in ((2 * 128 * 128, 128 * 128, 128, 1), (128 * 128, 128 * 128, 128, 1),
+               (2 * 128 * 136, 128 * 136, 136, 1)):
+        test_backward_ext_rejects_bad_options(lib, _ext_db(stride=st), bnd.SDPA_ERR_HIP, "")
+    q, k, v, out = _t(), _t(), _t(), _t(data=FAKE_OUT)
+    s_, o_ = ctypes.c_uint64(), ctypes.c_uint64()
+    rc = lib.sdpa_fwd_ext(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0.1, 1, math.nan,
+                          ctypes.byref(out), FAKE_LSE, ctypes.byref(s_), ctypes.byref(o_),
+                          ctypes.byref(_ext_db(data=FAKE)), None)
+    assert rc == bnd.SDPA_ERR_HIP, _err(lib)
+
+
 def test_workspace_size():
     # 8 bytes per query row (D and the base-2 LSE), rounded up to 256 bytes.
     assert sdpa.sdpa_bwd_workspace_size(1, 2, 128) == 2048
