@@ -6,7 +6,9 @@ b2 h12 s1024 d64 causal bf16 workload (the shape of the nvFuser test
 
 Prints ONE JSON line:
   value         whole-step TFLOP/s, counted FLOPs (forward 4*B*H*Sq*Sk*E, halved
-                when causal; backward 2.5x forward) over the timed step time
+                when causal; backward 2.5x forward) over the timed step time: K
+                steps as replays of a HIP graph of up to 20 back-to-back steps
+                (ms_per_step_one_step_graph: a graph of one step, replayed K times)
   fwd / bwd     the same for the forward and the backward alone, each timed as
                 a HIP graph of back-to-back calls replayed between events on the
                 launch stream, and their fraction of the bf16 dense MFMA peak
@@ -265,11 +267,18 @@ def main():
     log("warm-up done")
 
     # The step's kernels replayed from a HIP graph captured once: the timed work
-    # is the same forward and backward, without the Python launch path.
+    # is the same forward and backward, without the Python launch path.  The
+    # graph holds n_graph back-to-back steps (the largest divisor of K up to
+    # 20), so the K timed steps are K / n_graph replays: each graph launch
+    # leaves the GPU idle for several microseconds at its boundary, which a
+    # training step's graph (many layers per launch) does not pay per
+    # attention call.  The one-step graph is timed beside it.
     # (With dropout every replay reuses the captured seed and offset.)
     # Capture and the eager reference start from the same RNG state (a replay
     # reuses the captured seed and offset).
-    graph = capture(step, lambda: sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset))
+    n_graph = max(d for d in range(1, min(args.steps, 20) + 1) if args.steps % d == 0)
+    graph = capture(lambda: [step() for _ in range(n_graph)],
+                    lambda: sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset))
     sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset)
     step()
     eager = [t.clone() for t in (out, lse, dq, dk, dv)]
@@ -280,8 +289,11 @@ def main():
     same = all(torch.equal(a, b) for a, b in zip(eager, (out, lse, dq, dk, dv)))
     if not same:
         raise RuntimeError("graph replay differs from the eager step")
-    ms_step = timed_loop(graph.replay, args.steps)
-    log(f"timed {args.steps} graph-replayed steps: {ms_step * 1e3:.2f} us/step")
+    ms_step = timed_loop(graph.replay, args.steps // n_graph) / n_graph
+    log(f"timed {args.steps} graph-replayed steps ({n_graph} per graph): {ms_step * 1e3:.2f} us/step")
+    graph1 = capture(step, lambda: sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset))
+    ms_step_1 = timed_loop(graph1.replay, args.steps)
+    log(f"timed {args.steps} one-step graph replays: {ms_step_1 * 1e3:.2f} us/step")
     ms_eager = timed_loop(step, args.steps)
     log(f"timed {args.steps} eager steps: {ms_eager * 1e3:.2f} us/step")
     # Forward-only and backward-only: graphs of back-to-back launches replayed
@@ -399,8 +411,12 @@ def main():
                    "layout": w.layout, "causal": w.causal, "dropout_p": w.dropout_p,
                    "bias": args.bias, "dbias": bool(args.dbias), "keep_bits": bool(args.keep_bits),
                    "cache": "warm (same buffers every step)"},
-        "timing": "graph replay of the captured step (eager_ms_per_step: the same step "
+        "timing": f"replays of a HIP graph of {n_graph} back-to-back steps, K / {n_graph} "
+                  "replays between events on the launch stream (ms_per_step_one_step_graph: "
+                  "a graph of one step replayed K times; eager_ms_per_step: the same step "
                   "issued from Python each time)",
+        "steps_per_graph": n_graph,
+        "ms_per_step_one_step_graph": ms_step_1,
         "eager_ms_per_step": ms_eager,
         "fwd": {"tflops": f_fwd / (ms_fwd * 1e-3) / 1e12, "us": ms_fwd * 1e3,
                 "frac_peak": f_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
