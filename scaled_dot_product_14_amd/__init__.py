@@ -8,8 +8,11 @@ declared in ``include/sdpa14.h``); this package is its thin Python binding.
 
 Tensors are bf16 or fp16, logical [B, H, S, E], BHSE or BSHE stride order, E a
 multiple of 8 up to 128.
-``sdpa_fwd_ext`` / ``sdpa_bwd_ext`` add head sharding of the dropout stream and
-a device-resident RNG state for captured graphs.
+``sdpa_fwd_ext`` / ``sdpa_bwd_ext`` add head sharding of the dropout stream, a
+device-resident RNG state for captured graphs, an additive bias and its
+gradient (``dbias``), a dropout keep-bit cache, an inference-only forward and
+launching the backward's two kernels apart.  ``sdpa_bwd_noalloc`` is the
+backward for callers that cannot allocate device memory.
 """
 
 from ._binding import (  # noqa: F401
