@@ -122,3 +122,58 @@ def test_bias_gradient_with_the_allocation_free_backward():
     assert torch.equal(d1, d2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_bias_gradient_in_a_permuted_layout():
+    # dbias laid out [B, Sq, H, Sk] in memory (logical [B, H, Sq, Sk]): the
+    # kernels take any non-overlapping strides.
+    B, H, Sq, Sk, E = 2, 3, 160, 200, 64
+    q, k, v, do = workloads.draw(B, H, Sq, Sk, E, 74, 1.0, "BSHE", device="cuda")
+    bias = _bias((B, H, Sq, Sk), 75, torch.bfloat16)
+    out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, 0.0, True, bias=bias)
+    mem = torch.full((B, Sq, H, Sk), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dbias = mem.transpose(1, 2)
+    sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, 0.0, True, s, o, bias=bias, dbias=dbias)
+    ref, _ = _nan_grad(B, H, Sq, Sk, torch.bfloat16)
+    sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, 0.0, True, s, o, bias=bias, dbias=ref)
+    torch.cuda.synchronize()
+    assert torch.equal(dbias, ref)
+
+
+def test_bias_gradient_in_a_captured_graph():
+    # The backward with dbias captured once and replayed three times, with
+    # eager work between the replays; every replay matches the eager call.
+    B, H, S, E = 1, 4, 256, 64
+    q, k, v, do = workloads.draw(B, H, S, S, E, 76, 1.0, "BHSE", device="cuda")
+    bias = _bias((1, H, S, S), 77, torch.bfloat16)
+    out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, 0.0, True, bias=bias)
+    dq, dk, dv = (torch.empty_like(t) for t in (q, k, v))
+    ws = torch.empty(sdpa.sdpa_bwd_workspace_size(B, H, S), dtype=torch.uint8, device="cuda")
+    dbias, _ = _nan_grad(B, H, S, S, torch.bfloat16)
+
+    def call():
+        sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, 0.0, True, s, o, None, dq, dk, dv, ws,
+                          bias=bias, dbias=dbias)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (dq, dk, dv, dbias)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (dq, dk, dv, dbias):
+            t.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk).item()
+        for a, b in zip((dq, dk, dv, dbias), eager):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager call"
