@@ -73,8 +73,9 @@ def log(msg):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "fwd": ["fwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h", "occupancy.h"],
-    "bwd_main": ["bwd.hip", "lds_ring.h", "device_common.h", "philox.h", "kernels.h"],
-    "bwd_rows": ["bwd.hip", "device_common.h", "kernels.h"],
+    "bwd_main": ["bwd.hip", "bwd_e128.hip", "bwd_kernels.h", "lds_ring.h", "device_common.h",
+                 "philox.h", "kernels.h"],
+    "bwd_rows": ["bwd.hip", "bwd_kernels.h", "device_common.h", "kernels.h"],
 }
 
 

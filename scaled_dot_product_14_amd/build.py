@@ -21,7 +21,12 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libsdpa14.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["sdpa14_api.hip", "fwd.hip", "bwd.hip", "mask.hip", "rng.hip"]
+SOURCES = ["sdpa14_api.hip", "fwd.hip", "bwd.hip", "bwd_e128.hip", "mask.hip", "rng.hip"]
+# Per-source additions.  The head-dim-128 backward main kernel runs one wave
+# per SIMD; LLVM's iterative-ILP scheduler (registers traded for
+# instruction-level parallelism) measured 10% faster there, and slower for the
+# head-dim-64 kernels, which share each SIMD between two waves.
+EXTRA_FLAGS = {"bwd_e128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 ARCH = "gfx950"
 # Device code: packed fp32 VALU instructions are switched off; MFMA accumulators
@@ -52,7 +57,8 @@ def hipcc_path() -> str:
 
 
 def _compile(hipcc: str, src: str, obj: str, verbose: bool) -> None:
-    cmd = [hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in res.stderr.splitlines() if noise not in ln)

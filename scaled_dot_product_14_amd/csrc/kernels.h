@@ -81,6 +81,9 @@ hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
 hipError_t launch_bwd_rows(const BwdParams& p, bool f16, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdParams& p, bool causal, bool dropout, bool f16,
                            hipStream_t stream);
+// The main kernel at tile head dim 128 (its own translation unit).
+hipError_t launch_bwd_main_e128(const BwdParams& p, bool causal, bool dropout, bool f16,
+                                hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 // Words per row of the keep-bit cache: bit j % 32 of word j / 32 is key j's bit.
 inline int keep_words(int64_t Sk) { return (int)(((Sk + 31) / 32 + 3) / 4 * 4); }
