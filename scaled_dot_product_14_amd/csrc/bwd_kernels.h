@@ -383,6 +383,10 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
       }
     }
     if (active) {
+      // At head dim 128 (one wave per SIMD) LLVM's exponential-interleaving
+      // instruction-group strategy measured 3% faster; it changes only the
+      // instruction order.
+      if constexpr (E == 128) __builtin_amdgcn_iglp_opt(2);
       const unsigned char* st = lds + ring_offset<C::STAGE_A>(it);
       const unsigned char* tq = st + ST_Q + qs * TILE_B;
       const unsigned char* tdo = st + ST_DO + qs * TILE_B;
@@ -686,6 +690,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     // stage they fetch rows nobody reads).
     if (!active) issue(it + 2);
     if (active) {
+      if constexpr (E == 128) __builtin_amdgcn_iglp_opt(2);  // as in the dK/dV role
       const unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
       const unsigned char* tk = st + ST_K + ks * TILE_B;
       const unsigned char* tv = st + ST_V + ks * TILE_B;
