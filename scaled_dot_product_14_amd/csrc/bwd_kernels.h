@@ -528,8 +528,13 @@ __device__ __forceinline__ void role_dkdv(const BwdParams& p, int bh, int kblk,
 }
 
 // ---------------------------------------------------------------------------
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP>
+// NST: stages in the ring.  Three (the default) keep the loads two steps
+// ahead and take the block's Q, dO, -D and L through a third stage; two leave
+// room for a second workgroup per CU at head dim 128, load those straight
+// into registers and keep the loads one step ahead.
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP, int NST = 3>
 __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, unsigned char* lds) {
+  static_assert(NST == 2 || NST == 3, "ring depth");
   using C = BwdCfg<E, BIAS, KEEP>;
   constexpr int NES = C::NES, NEB = C::NEB, NLD = C::NLD, TILE_B = C::TILE_B;
   constexpr int ST_K = 0, ST_V = 2 * TILE_B, ST_BIAS = 4 * TILE_B, ST_KEEP = ST_BIAS + C::BIAS_B;
@@ -590,7 +595,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
   // Load idx (0 .. NPAIR_B-1) of stage it: (half, tensor, k) for the K and V
   // tiles, then the two loads of the bias block.
   auto issue_one = [&](int it, int idx, float after) {
-    unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
+    unsigned char* st = lds + ring_offset<C::STAGE_B, NST>(it);
     if (BIAS && idx >= 4 * NLD && idx < 4 * NLD + C::NBL) {
       const int k = idx - 4 * NLD;
       dma16_after(br, st + ST_BIAS + k * 4096 + wave * 1024, (uint32_t)(128 * it) + obias[k],
@@ -641,9 +646,31 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     drow = philox_row_base(drop, dropout_head(drop, b, h), p.Sq, qrow, sk4);
   }
 
+  // The B operands of S^T = K Q^T and dP^T = V dO^T: each wave's rows of Q and
+  // dO, lane = row, e = 16*es + 8*g + 0..7; and the row's -D and L.
+  bf16x8 qf[NES], dof[NES];
+  float ndsum, lse2;
+  if constexpr (NST == 2) {
+    // Straight from memory into registers; rows past Sq and columns past the
+    // head dim read as zeros through the buffer range check.
+#pragma unroll
+    for (int es = 0; es < NES; ++es) {
+      const uint32_t col = (uint32_t)(16 * es + 8 * g);
+      const uint32_t oob = (int)col < p.E ? 0u : 0x80000000u;
+      qf[es] = __builtin_bit_cast(
+          bf16x8, buffer_load16(rq, ((uint32_t)qrow * (uint32_t)(p.sq.s * 2) + 2u * col) | oob));
+      dof[es] = __builtin_bit_cast(
+          bf16x8, buffer_load16(rdo, ((uint32_t)qrow * (uint32_t)(p.sdo.s * 2) + 2u * col) | oob));
+    }
+    const int64_t row = (int64_t)bh * p.Sq + min(qrow, p.Sq - 1);
+    ndsum = p.dl[row];
+    lse2 = p.dl[(int64_t)p.B * p.H * p.Sq + row];
+    if (n_it > 0) issue(0);
+    ring_barrier<0>();
+  } else {
   // Q and dO of the block pass through stage 2 (first refilled by iteration 0)
   // together with the first two stages; each wave then takes its rows'
-  // fragments, the B operands of S^T = K Q^T and dP^T = V dO^T.
+  // fragments.
   {
     uint32_t oqq[NLD], odd[NLD];
 #pragma unroll
@@ -664,34 +691,34 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
     ring_barrier<C::NPAIR_B>();
   else
     ring_barrier<0>();
-  bf16x8 qf[NES], dof[NES];
 #pragma unroll
   for (int es = 0; es < NES; ++es) {
     qf[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_B + qsb * TILE_B, aoff[es]);
     dof[es] = lds_at<bf16x8>(lds + 2 * C::STAGE_B + (2 + qsb) * TILE_B, aoff[es]);
   }
-  // -D and L of the row; -D seeds dP's accumulator (without dropout).
-  const float ndsum = lds_at<float>(lds + 2 * C::STAGE_B + 4 * TILE_B, (qsb * 32 + l32) * 4);
-  const float lse2 = lds_at<float>(lds + 2 * C::STAGE_B + 4 * TILE_B + 256, (qsb * 32 + l32) * 4);
-  f32x16 dinit;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) dinit[r] = DROPOUT ? 0.f : ndsum;
+  ndsum = lds_at<float>(lds + 2 * C::STAGE_B + 4 * TILE_B, (qsb * 32 + l32) * 4);
+  lse2 = lds_at<float>(lds + 2 * C::STAGE_B + 4 * TILE_B + 256, (qsb * 32 + l32) * 4);
   if (n_it > 1) issue(1);
   if (n_it > 1)
     ring_barrier<C::NPAIR_B>();
   else
     ring_barrier<0>();
+  }
+  // -D seeds dP's accumulator (without dropout).
+  f32x16 dinit;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = DROPOUT ? 0.f : ndsum;
 
   for (int it = 0; it < n_it; ++it) {
     const int j = 2 * it + ks;
     const int k0 = j * 32;
     const bool active = !(j >= kt_end || (CAUSAL && k0 > q0 + 31));
-    // Loads of stage it+2 on every step, as in the dK/dV role (past the last
-    // stage they fetch rows nobody reads).
-    if (!active) issue(it + 2);
+    // Loads of stage it+NST-1 on every step, as in the dK/dV role (past the
+    // last stage they fetch rows nobody reads).
+    if (!active) issue(it + NST - 1);
     if (active) {
       if constexpr (E == 128) __builtin_amdgcn_iglp_opt(2);  // as in the dK/dV role
-      const unsigned char* st = lds + ring_offset<C::STAGE_B>(it);
+      const unsigned char* st = lds + ring_offset<C::STAGE_B, NST>(it);
       const unsigned char* tk = st + ST_K + ks * TILE_B;
       const unsigned char* tv = st + ST_V + ks * TILE_B;
 
@@ -719,7 +746,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
         sacc = mfma16<F16>(lds_at<bf16x8>(tk, aoff[es]), qf[es], sacc);
         dpacc = mfma16<F16>(lds_at<bf16x8>(tv, aoff[es]), dof[es], dpacc);
       }
-      issue_slot(it + 2, 0, 0.f);
+      issue_slot(it + NST - 1, 0, 0.f);
 
       // Only tiles that reach the diagonal or past Sk take the masked variant.
       const bool need_mask = (k0 + 31 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1));
@@ -750,7 +777,7 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
             float dp = dpacc[r];  // dP - D without dropout
             if (DROPOUT) dp = (((kbits >> u) & 1) ? dp * drop.keep_scale : 0.f) + ndsum;
             dsb[r >> 3][r & 7] = to16<F16>(ps * dp);
-            if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + 2, 1 + cg / 2, ps);
+            if (u == 3 && (cg == 1 || cg == 3)) issue_slot(it + NST - 1, 1 + cg / 2, ps);
           }
         }
       };
@@ -765,10 +792,14 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
         for (int hf = 0; hf < 2; ++hf) {
           const int o0 = troff[0][eb] + hf * 16 * C::ROW_B, o1 = troff[1][eb] + hf * 16 * C::ROW_B;
           dqa[eb] = mfma16<F16>(tr_pair(tk, o0, o1), dsb[hf], dqa[eb]);
-          if (hf == 1 && eb == 0) issue_slot(it + 2, 3, 0.f);
+          if (hf == 1 && eb == 0) issue_slot(it + NST - 1, 3, 0.f);
         }
     }
-    ring_barrier<C::NPAIR_B>();
+    // Stage it+1 must have landed (with two stages it went out in this step).
+    if constexpr (NST == 3)
+      ring_barrier<C::NPAIR_B>();
+    else
+      ring_barrier<0>();
   }
   ring_barrier<0>();  // the trailing loads have landed before the stages are reused
 
@@ -793,10 +824,23 @@ struct BwdOrder {
 // Workgroup order: per head, blocks in BwdOrder order (or, past kMaxOrder
 // blocks, dK/dV and dQ alternating, heaviest causal blocks first); all blocks
 // of a head sit on one XCD when the head count allows.
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP, bool DBIAS>
+// ROLES: 3 compiles both workgroup roles, 2 only the dQ role with a two-stage
+// ring (so that two of its workgroups share a CU at head dim 128).  `order`
+// says how a workgroup finds its block: 1 from the table `ord`, 0 dK/dV and dQ
+// blocks alternating (past kMaxOrder blocks), 2 every block a dK/dV block and
+// 3 every block a dQ block, rank = slot (launches of one role, past
+// kMaxOrder blocks).
+template <int E, bool BIAS, bool KEEP, int ROLES>
+constexpr int bwd_lds_bytes() {
+  using C = BwdCfg<E, BIAS, KEEP>;
+  return ROLES == 2 ? (2 * C::STAGE_B > C::RED_B / 2 ? 2 * C::STAGE_B : C::RED_B / 2) : C::LDS_B;
+}
+
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP, bool DBIAS,
+          int ROLES = 3>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb, BwdOrder ord,
-                                                  int use_order) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[BwdCfg<E, BIAS, KEEP>::LDS_B];
+                                                  int order) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[bwd_lds_bytes<E, BIAS, KEEP, ROLES>()];
   const int bh_count = p.B * p.H;
   int bh, slot;
   if ((bh_count & 7) == 0) {
@@ -810,10 +854,13 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb,
   }
   bool dkdv;
   int rank;
-  if (use_order) {
+  if (order == 1) {
     const int e = ord.item[slot];
     dkdv = (e & 0x8000) == 0;
     rank = e & 0x7FFF;
+  } else if (order >= 2) {
+    dkdv = order == 2;
+    rank = slot;
   } else {
     const int m = min(nkb, nqb);
     if (slot < 2 * m) {
@@ -824,10 +871,14 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb,
       rank = slot - m;
     }
   }
-  if (dkdv)
-    role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16, KEEP, DBIAS>(p, bh, rank, lds);
-  else
-    role_dq<E, CAUSAL, DROPOUT, BIAS, F16, KEEP>(p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
+  if constexpr (ROLES == 3) {
+    if (dkdv) {
+      role_dkdv<E, CAUSAL, DROPOUT, BIAS, F16, KEEP, DBIAS>(p, bh, rank, lds);
+      return;
+    }
+  }
+  role_dq<E, CAUSAL, DROPOUT, BIAS, F16, KEEP, ROLES == 2 ? 2 : 3>(
+      p, bh, CAUSAL ? nqb - 1 - rank : rank, lds);
 }
 
 // -D_i = -rowsum(dO * O) and L_i = LSE_i * log2(e) - log2(scale) for every
@@ -874,13 +925,28 @@ hipError_t launch_rows_t(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// At head dim 128, without dropout or a bias, the two roles go out as two
+// launches: the dK/dV blocks (one workgroup per CU, as their registers
+// require; the two-role kernel, whose code for that role measured faster than
+// a one-role build) and then the dQ blocks with a two-stage ring, two
+// workgroups per CU (3.5% faster at b1 h32 q4096 k8192 than one launch).
+// Dropout's registers and a bias's LDS leave the dQ kernel one workgroup per
+// CU, so those variants, and head dim 64, keep one launch for both roles.
+template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
+constexpr bool bwd_split_roles() {
+  return E == 128 && !DROPOUT && !BIAS;
+}
+
 template <int E, bool F16>
 hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
+  const bool split = E == 128 && !dropout && p.bias == nullptr;
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
-  const dim3 grid((unsigned)(nkb + nqb) * (unsigned)(p.B * p.H));
-  BwdOrder ord;
-  const int use_order = nkb + nqb <= kMaxOrder ? 1 : 0;
-  if (use_order) {
+  const unsigned bhn = (unsigned)(p.B * p.H);
+  BwdOrder ord, ordk, ordq;
+  const int use_order = !split && nkb + nqb <= kMaxOrder ? 1 : 0;
+  const int use_k = split && nkb <= kMaxOrder ? 1 : 0;
+  const int use_q = split && nqb <= kMaxOrder ? 1 : 0;
+  if (use_order || use_k || use_q) {
     // Estimated run of a block: steps times a measured per-step cost plus a
     // fixed prologue/epilogue (dK/dV: ~1.5 us per step + ~4 us; dQ: ~1.1 us +
     // ~3.3 us, at b2 h12 s1024 d64), in units of 0.1 us.
@@ -901,13 +967,26 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStrea
     }
     std::stable_sort(items.begin(), items.end(),
                      [](const Item& a, const Item& b) { return a.cost > b.cost; });
-    for (size_t i = 0; i < items.size(); ++i) ord.item[i] = (uint16_t)items[i].key;
+    int n = 0, nk = 0, nq = 0;
+    for (const Item& it : items) {
+      if (use_order) ord.item[n++] = (uint16_t)it.key;
+      if (use_k && (it.key & 0x8000) == 0) ordk.item[nk++] = (uint16_t)it.key;
+      if (use_q && (it.key & 0x8000) != 0) ordq.item[nq++] = (uint16_t)it.key;
+    }
   }
   auto go3 = [&](auto c, auto d, auto bias, auto keep, auto db) {
-    hipLaunchKernelGGL((bwd_kernel<E, decltype(c)::value, decltype(d)::value,
-                                   decltype(bias)::value, F16, decltype(keep)::value,
-                                   decltype(db)::value>),
-                       grid, dim3(256), 0, stream, p, nkb, nqb, ord, use_order);
+    constexpr bool Cf = decltype(c)::value, Df = decltype(d)::value, Bf = decltype(bias)::value;
+    constexpr bool Kf = decltype(keep)::value, DBf = decltype(db)::value;
+    if constexpr (bwd_split_roles<E, Cf, Df, Bf>()) {
+      hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>), dim3((unsigned)nkb * bhn),
+                         dim3(256), 0, stream, p, nkb, nqb, ordk, use_k ? 1 : 2);
+      hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 2>), dim3((unsigned)nqb * bhn),
+                         dim3(256), 0, stream, p, nkb, nqb, ordq, use_q ? 1 : 3);
+    } else {
+      hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>),
+                         dim3((unsigned)(nkb + nqb) * bhn), dim3(256), 0, stream, p, nkb, nqb, ord,
+                         use_order);
+    }
   };
   auto go2 = [&](auto c, auto d, auto bias, auto keep) {
     if constexpr (decltype(bias)::value) {

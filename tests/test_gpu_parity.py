@@ -122,6 +122,11 @@ EXTRA = [
     # problem with dropout, and a non-causal BSHE case with Sq < Sk.
     (2, 3, 1024, 1024, 64, "BHSE", True, 0.1, 20),
     (1, 4, 512, 2048, 64, "BSHE", False, 0.0, 21),
+    # Head dim 128 without dropout or bias runs the backward's two roles as
+    # two launches (the dQ one with a two-stage ring): BSHE, causal with
+    # Sq > Sk and ragged lengths, several heads and batches.
+    (2, 3, 257, 200, 128, "BSHE", True, 0.0, 22),
+    (1, 2, 190, 700, 128, "BHSE", False, 0.0, 23),
 ]
 
 
