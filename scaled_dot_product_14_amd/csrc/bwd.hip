@@ -16,11 +16,11 @@ hipError_t launch_bwd_rows(const BwdParams& p, bool f16, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_main(const BwdParams& p, bool causal, bool dropout, bool f16,
-                           hipStream_t stream) {
+                           const TileChoice& tiles, hipStream_t stream) {
   const int E = tile_head_dim(p.E);
-  if (E == 128) return launch_bwd_main_e128(p, causal, dropout, f16, stream);
-  return f16 ? launch_main_t<64, true>(p, causal, dropout, stream)
-             : launch_main_t<64, false>(p, causal, dropout, stream);
+  if (E == 128) return launch_bwd_main_e128(p, causal, dropout, f16, tiles, stream);
+  return f16 ? launch_main_t<64, true>(p, causal, dropout, tiles, stream)
+             : launch_main_t<64, false>(p, causal, dropout, tiles, stream);
 }
 
 }  // namespace sdpa14

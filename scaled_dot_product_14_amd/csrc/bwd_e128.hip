@@ -12,9 +12,9 @@
 namespace sdpa14 {
 
 hipError_t launch_bwd_main_e128(const BwdParams& p, bool causal, bool dropout, bool f16,
-                                hipStream_t stream) {
-  return f16 ? launch_main_t<128, true>(p, causal, dropout, stream)
-             : launch_main_t<128, false>(p, causal, dropout, stream);
+                                const TileChoice& tiles, hipStream_t stream) {
+  return f16 ? launch_main_t<128, true>(p, causal, dropout, tiles, stream)
+             : launch_main_t<128, false>(p, causal, dropout, tiles, stream);
 }
 
 }  // namespace sdpa14

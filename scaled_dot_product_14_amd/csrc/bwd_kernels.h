@@ -52,6 +52,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_ring.h"
+#include "occupancy.h"
 
 namespace sdpa14 {
 namespace {
@@ -925,23 +926,37 @@ hipError_t launch_rows_t(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// At head dim 128, without dropout or a bias, the two roles go out as two
-// launches: the dK/dV blocks (one workgroup per CU, as their registers
-// require; the two-role kernel, whose code for that role measured faster than
-// a one-role build) and then the dQ blocks with a two-stage ring, two
-// workgroups per CU (3.5% faster at b1 h32 q4096 k8192 than one launch).
-// Dropout's registers and a bias's LDS leave the dQ kernel one workgroup per
-// CU, so those variants, and head dim 64, keep one launch for both roles.
-template <int E, bool CAUSAL, bool DROPOUT, bool BIAS>
-constexpr bool bwd_split_roles() {
-  return E == 128 && !DROPOUT && !BIAS;
+// Large problems without dropout or a bias run the two roles as two
+// launches: the dK/dV blocks (the two-role kernel given only dK/dV blocks,
+// whose code for that role measured faster than a one-role build) and then
+// the dQ blocks with a two-stage ring, which leaves room for more dQ
+// workgroups per CU: two instead of one at head dim 128, three instead of two
+// at 64.  The second launch starts only when the first has drained, so this
+// pays off only once each role fills the chip for several rounds: measured,
+// from 2 rounds of the one-launch kernel's slots at head dim 128 (1932 vs
+// 2062 us at b1 h32 q4096 k8192; 56 vs 50 us at b2 h12 s1024) and from 8 at
+// head dim 64 (298 vs 328 us at 8x16x2048^2 causal, no change at 4 rounds).
+// Dropout's registers and a bias's LDS would leave the dQ launch no more
+// workgroups per CU, so those variants keep one launch.
+template <int E, bool DROPOUT, bool BIAS>
+constexpr bool bwd_can_split() {
+  return !DROPOUT && !BIAS;
 }
 
 template <int E, bool F16>
-hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStream_t stream) {
-  const bool split = E == 128 && !dropout && p.bias == nullptr;
+hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, const TileChoice& tiles,
+                         hipStream_t stream) {
   const int nkb = (p.Sk + 63) / 64, nqb = (p.Sq + 63) / 64;
   const unsigned bhn = (unsigned)(p.B * p.H);
+  bool split = false;
+  if (!dropout && p.bias == nullptr) {
+    if (tiles.bwd_roles == 1 || tiles.bwd_roles == 2) {
+      split = tiles.bwd_roles == 2;
+    } else {
+      const long slots = (long)device_cus() * (E == 64 ? 2 : 1);  // one-launch residency
+      split = slots > 0 && (long)std::min(nkb, nqb) * bhn >= (E == 64 ? 8 : 2) * slots;
+    }
+  }
   BwdOrder ord, ordk, ordq;
   const int use_order = !split && nkb + nqb <= kMaxOrder ? 1 : 0;
   const int use_k = split && nkb <= kMaxOrder ? 1 : 0;
@@ -977,16 +992,18 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, hipStrea
   auto go3 = [&](auto c, auto d, auto bias, auto keep, auto db) {
     constexpr bool Cf = decltype(c)::value, Df = decltype(d)::value, Bf = decltype(bias)::value;
     constexpr bool Kf = decltype(keep)::value, DBf = decltype(db)::value;
-    if constexpr (bwd_split_roles<E, Cf, Df, Bf>()) {
-      hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>), dim3((unsigned)nkb * bhn),
-                         dim3(256), 0, stream, p, nkb, nqb, ordk, use_k ? 1 : 2);
-      hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 2>), dim3((unsigned)nqb * bhn),
-                         dim3(256), 0, stream, p, nkb, nqb, ordq, use_q ? 1 : 3);
-    } else {
-      hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>),
-                         dim3((unsigned)(nkb + nqb) * bhn), dim3(256), 0, stream, p, nkb, nqb, ord,
-                         use_order);
+    if constexpr (bwd_can_split<E, Df, Bf>()) {
+      if (split) {
+        hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>), dim3((unsigned)nkb * bhn),
+                           dim3(256), 0, stream, p, nkb, nqb, ordk, use_k ? 1 : 2);
+        hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 2>), dim3((unsigned)nqb * bhn),
+                           dim3(256), 0, stream, p, nkb, nqb, ordq, use_q ? 1 : 3);
+        return;
+      }
     }
+    hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>),
+                       dim3((unsigned)(nkb + nqb) * bhn), dim3(256), 0, stream, p, nkb, nqb, ord,
+                       use_order);
   };
   auto go2 = [&](auto c, auto d, auto bias, auto keep) {
     if constexpr (decltype(bias)::value) {

@@ -68,6 +68,8 @@ struct TileChoice {
   int fwd_shape;  // forward workgroup: 1 = 4 query sub-tiles, 2 = 2 sub-tiles x 2 key
                   // shares, 3 = 1 sub-tile x 4 key shares (32 query rows per sub-tile),
                   // 4 = causal split launch (kinds 3 with 32-key tiles and 2, head dim 64)
+  int bwd_roles;  // backward main pass: 1 = both roles in one launch, 2 = dK/dV and dQ
+                  // blocks as two launches (no dropout, no bias; else one launch)
 };
 
 // Tile head dim of the kernels that run head dim E (a multiple of 8, at most 128).
@@ -80,10 +82,10 @@ hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
 // H, Sq) bytes), then the main kernel, launched in that order on one stream.
 hipError_t launch_bwd_rows(const BwdParams& p, bool f16, hipStream_t stream);
 hipError_t launch_bwd_main(const BwdParams& p, bool causal, bool dropout, bool f16,
-                           hipStream_t stream);
+                           const TileChoice& tiles, hipStream_t stream);
 // The main kernel at tile head dim 128 (its own translation unit).
 hipError_t launch_bwd_main_e128(const BwdParams& p, bool causal, bool dropout, bool f16,
-                                hipStream_t stream);
+                                const TileChoice& tiles, hipStream_t stream);
 size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 // Words per row of the keep-bit cache: bit j % 32 of word j / 32 is key j's bit.
 inline int keep_words(int64_t Sk) { return (int)(((Sk + 31) / 32 + 3) / 4 * 4); }

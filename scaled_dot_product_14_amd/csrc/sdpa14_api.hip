@@ -368,10 +368,13 @@ bool forced_launch_failure(const char* what) {
 // four sub-tiles, two by two, one sub-tile with four key shares, the causal
 // split launch) forces one, read on every call so that a process can compare
 // them.  A shape the problem cannot take (3 at head dim 128, 4 without causal
-// masking or at head dim 128) runs two by two.
+// masking or at head dim 128) runs two by two.  SDPA14_BWD_ROLES (1: one
+// launch, 2: two) does the same for the backward main pass; two launches need
+// a call without dropout or bias, else it runs one.
 TileChoice tile_choice() {
-  TileChoice t{0};
+  TileChoice t{0, 0};
   if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
+  if (const char* s = getenv("SDPA14_BWD_ROLES")) t.bwd_roles = atoi(s);
   return t;
 }
 
@@ -667,7 +670,7 @@ int bwd_call(const sdpa_tensor* dout, const sdpa_tensor* q, const sdpa_tensor* k
     err = timed_launch(SDPA_KERNEL_BWD_ROWS, st, [&] { return launch_bwd_rows(p, f16, st); });
   if (err == hipSuccess && (e.bwd_parts & 2))
     err = timed_launch(SDPA_KERNEL_BWD, st,
-                       [&] { return launch_bwd_main(p, causal, drop, f16, st); });
+                       [&] { return launch_bwd_main(p, causal, drop, f16, tile_choice(), st); });
   return hip_status(err, "backward launch");
 }
 
