@@ -274,14 +274,17 @@ def main():
     # leaves the GPU idle for several microseconds at its boundary, which a
     # training step's graph (many layers per launch) does not pay per
     # attention call.  The one-step graph is timed beside it.
-    # (With dropout every replay reuses the captured seed and offset.)
-    # Capture and the eager reference start from the same RNG state (a replay
-    # reuses the captured seed and offset).
+    # With dropout each captured step draws the next offset from the host RNG
+    # state and every replay reuses those captured offsets, so the eager
+    # reference runs the same n_graph steps from the same starting state: the
+    # buffers then hold the last step's results on both sides.
     n_graph = max(d for d in range(1, min(args.steps, 20) + 1) if args.steps % d == 0)
     graph = capture(lambda: [step() for _ in range(n_graph)],
                     lambda: sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset))
     sdpa.sdpa_set_rng_state(w.rng_seed, w.rng_offset)
-    step()
+    for _ in range(n_graph):
+        step()
+    torch.cuda.synchronize()
     eager = [t.clone() for t in (out, lse, dq, dk, dv)]
     for t in (out, dq, dk, dv):
         t.zero_()
