@@ -958,9 +958,12 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, const Ti
     }
   }
   BwdOrder ord, ordk, ordq;
-  const int use_order = !split && nkb + nqb <= kMaxOrder ? 1 : 0;
-  const int use_k = split && nkb <= kMaxOrder ? 1 : 0;
-  const int use_q = split && nqb <= kMaxOrder ? 1 : 0;
+  // Past kMaxOrder blocks (or when asked to) the blocks go out in an order the
+  // kernel computes from the block index instead of the table.
+  const bool table = tiles.bwd_order != 1;
+  const int use_order = table && !split && nkb + nqb <= kMaxOrder ? 1 : 0;
+  const int use_k = table && split && nkb <= kMaxOrder ? 1 : 0;
+  const int use_q = table && split && nqb <= kMaxOrder ? 1 : 0;
   if (use_order || use_k || use_q) {
     // Estimated run of a block: steps times a measured per-step cost plus a
     // fixed prologue/epilogue (dK/dV: ~1.5 us per step + ~4 us; dQ: ~1.1 us +

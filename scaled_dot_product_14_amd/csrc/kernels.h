@@ -70,6 +70,8 @@ struct TileChoice {
                   // 4 = causal split launch (kinds 3 with 32-key tiles and 2, head dim 64)
   int bwd_roles;  // backward main pass: 1 = both roles in one launch, 2 = dK/dV and dQ
                   // blocks as two launches (no dropout, no bias; else one launch)
+  int bwd_order;  // backward dispatch order: 1 = the arithmetic order that problems past
+                  // the order table's size use, whatever the size
 };
 
 // Tile head dim of the kernels that run head dim E (a multiple of 8, at most 128).

@@ -370,11 +370,14 @@ bool forced_launch_failure(const char* what) {
 // them.  A shape the problem cannot take (3 at head dim 128, 4 without causal
 // masking or at head dim 128) runs two by two.  SDPA14_BWD_ROLES (1: one
 // launch, 2: two) does the same for the backward main pass; two launches need
-// a call without dropout or bias, else it runs one.
+// a call without dropout or bias, else it runs one.  SDPA14_BWD_ORDER=1 deals
+// the backward's blocks in the order computed from the block index, which
+// problems of more than 1024 key plus query blocks per head use, at any size.
 TileChoice tile_choice() {
-  TileChoice t{0, 0};
+  TileChoice t{0, 0, 0};
   if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
   if (const char* s = getenv("SDPA14_BWD_ROLES")) t.bwd_roles = atoi(s);
+  if (const char* s = getenv("SDPA14_BWD_ORDER")) t.bwd_order = atoi(s);
   return t;
 }
 

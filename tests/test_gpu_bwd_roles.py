@@ -87,3 +87,32 @@ def test_two_launches_chosen_for_a_large_problem(monkeypatch):
     ref = sdpa_ref.bwd(dc, qc, kc, vc, 0.0, True, heads=heads)
     sel = (tuple(b for b, _ in heads), tuple(h for _, h in heads))
     assert_grads([(n, host64(g)[sel], r[sel]) for n, g, r in zip(("dq", "dk", "dv"), auto, ref)])
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,dtype", CASES[:4])
+@pytest.mark.parametrize("p", [0.0, 0.1])
+def test_the_computed_order_gives_the_same_gradients(monkeypatch, B, H, Sq, Sk, E, layout,
+                                                     causal, dtype, p):
+    # Problems of more than 1024 key plus query blocks per head deal their
+    # blocks in an order computed from the block index (alternating roles, or
+    # one role per launch) instead of the host-built table; SDPA14_BWD_ORDER=1
+    # takes that path at any size.  A block is computed the same way whichever
+    # workgroup takes it, so the gradients are bitwise those of the table order.
+    say(f"backward order: B{B} H{H} Sq{Sq} Sk{Sk} E{E} {layout} causal={causal} {dtype} p={p}")
+    q, k, v, do = workloads.draw(B, H, Sq, Sk, E, 93, 1.0, layout, device="cuda")
+    q, k, v, do = (t.to(dtype) for t in (q, k, v, do))
+    sdpa.sdpa_set_rng_state(5, 64)
+    out, lse, s, o = sdpa.sdpa_fwd(q, k, v, p, causal)
+    for roles in (1, 2):
+        monkeypatch.setenv("SDPA14_BWD_ROLES", str(roles))
+        monkeypatch.delenv("SDPA14_BWD_ORDER", raising=False)
+        table = sdpa.sdpa_bwd(do, q, k, v, out, lse, p, causal, s, o)
+        monkeypatch.setenv("SDPA14_BWD_ORDER", "1")
+        computed = sdpa.sdpa_bwd(do, q, k, v, out, lse, p, causal, s, o)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), table, computed):
+            assert torch.equal(a, b), f"{name} differs between the two orders ({roles} launch(es))"
+    monkeypatch.delenv("SDPA14_BWD_ORDER", raising=False)
+    monkeypatch.delenv("SDPA14_BWD_ROLES", raising=False)
+    ref = sdpa_ref.bwd(do, q, k, v, p, causal, s, o)
+    assert_grads([(n, host64(g), r) for n, g, r in zip(("dq", "dk", "dv"), computed, ref)])
