@@ -6,7 +6,8 @@ E * 2 stays below 2^31 (the 255 rows cover loads issued past the last row,
 which the buffer range check turns into zeros).  Here every tensor, outputs
 included, is a view with the largest row stride that rule allows, so the
 last rows sit just below 2 GiB into their slice; the results must match the
-oracle on the logical values.  A stride one granule larger is refused.
+oracle on the logical values, and nothing may be written in the gaps between
+the rows.  A stride one granule larger is refused.
 """
 
 import pytest
@@ -38,7 +39,13 @@ def _wide(x, stride):
 
 def _empty_wide(S, E, stride, dtype):
     buf = torch.full(((S - 1) * stride + E,), float("nan"), dtype=dtype, device="cuda")
-    return buf.as_strided((1, 1, S, E), (buf.numel(), buf.numel(), stride, 1))
+    return buf.as_strided((1, 1, S, E), (buf.numel(), buf.numel(), stride, 1)), buf
+
+
+def _only_the_view_written(view, buf):
+    """Every element of the NaN-filled buffer outside the view is still NaN."""
+    written = int((~torch.isnan(buf)).sum().item())
+    assert written == view.numel(), f"{written} elements written, {view.numel()} in the view"
 
 
 @pytest.mark.parametrize("Sq,Sk,E,causal", [(300, 300, 64, True), (200, 333, 128, False),
@@ -50,10 +57,10 @@ def test_rows_just_below_two_gib(Sq, Sk, E, causal):
     q0, k0, v0, do0 = workloads.draw(1, 1, Sq, Sk, E, 91, 1.0, "BHSE", device="cuda")
     q, do = _wide(q0, sq_s), _wide(do0, sq_s)
     k, v = _wide(k0, sk_s), _wide(v0, sk_s)
-    out = _empty_wide(Sq, E, sq_s, torch.bfloat16)
-    dq = _empty_wide(Sq, E, sq_s, torch.bfloat16)
-    dk = _empty_wide(Sk, E, sk_s, torch.bfloat16)
-    dv = _empty_wide(Sk, E, sk_s, torch.bfloat16)
+    out, out_buf = _empty_wide(Sq, E, sq_s, torch.bfloat16)
+    dq, dq_buf = _empty_wide(Sq, E, sq_s, torch.bfloat16)
+    dk, dk_buf = _empty_wide(Sk, E, sk_s, torch.bfloat16)
+    dv, dv_buf = _empty_wide(Sk, E, sk_s, torch.bfloat16)
     o, lse, s, off = sdpa.sdpa_fwd(q, k, v, 0.0, causal, None, out=out)
     sdpa.sdpa_bwd(do, q, k, v, out, lse, 0.0, causal, s, off, None, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
@@ -63,7 +70,10 @@ def test_rows_just_below_two_gib(Sq, Sk, E, causal):
     assert_lse(host64(lse), ref_lse)
     assert_grads([("dq", host64(dq), ref_dq), ("dk", host64(dk), ref_dk),
                   ("dv", host64(dv), ref_dv)])
-    del q, k, v, do, out, dq, dk, dv
+    # Nothing is stored between the rows (the gaps stay NaN), nor past the last row.
+    for view, buf in ((out, out_buf), (dq, dq_buf), (dk, dk_buf), (dv, dv_buf)):
+        _only_the_view_written(view, buf)
+    del q, k, v, do, out, dq, dk, dv, out_buf, dq_buf, dk_buf, dv_buf
     torch.cuda.empty_cache()
 
 

@@ -4,7 +4,8 @@ Each case draws its shape and options from a fixed seed: batch and heads,
 query and key lengths from 1 to 400 (so most tiles are ragged), every head
 dim the kernels take (multiples of 8 up to 128), BHSE or BSHE strides, causal
 or not, dropout, an additive bias of several broadcast shapes, bf16 or fp16,
-an explicit softmax scale, and the forward workgroup shape and backward
+an explicit softmax scale, outputs given as padded views (whose spare
+columns must stay untouched), and the forward workgroup shape and backward
 launch form forced through SDPA14_FWD_SHAPE / SDPA14_BWD_ROLES.  The bars are
 the same as for the fixed parity cases.
 """
@@ -43,6 +44,7 @@ def _case(i):
         "fwd_shape": r.choice([0, 0, 1, 2, 3, 4]),
         "bwd_roles": r.choice([0, 0, 1, 2]),
         "seed": 500 + i,
+        "pad_out": r.random() < 0.5,
     }
     return c
 
@@ -71,9 +73,23 @@ def test_random_configuration(i, monkeypatch):
     rng = (c["seed"] * 13 + 1, c["seed"] * 5)
     sdpa.sdpa_set_rng_state(*rng)
     p, causal, scale = c["p"], c["causal"], c["scale"]
-    out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, p, causal, scale, bias=bias)
-    dq, dk, dv = sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, p, causal, s, o, scale, bias=bias)
+    pads = []
+    if c["pad_out"]:
+        # Outputs as NaN-filled views with 8 spare columns per row: the spare
+        # columns must stay NaN.
+        def padded(S):
+            buf = torch.full((B, H, S, E + 8), float("nan"), dtype=c["dtype"], device="cuda")
+            pads.append(buf)
+            return buf[..., :E]
+        out, dq, dk, dv = padded(Sq), padded(Sq), padded(Sk), padded(Sk)
+        out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, p, causal, scale, out=out, bias=bias)
+        sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, p, causal, s, o, scale, dq, dk, dv, bias=bias)
+    else:
+        out, lse, s, o = sdpa.sdpa_fwd_ext(q, k, v, p, causal, scale, bias=bias)
+        dq, dk, dv = sdpa.sdpa_bwd_ext(do, q, k, v, out, lse, p, causal, s, o, scale, bias=bias)
     torch.cuda.synchronize()
+    for buf in pads:
+        assert torch.isnan(buf[..., E:]).all().item(), "a kernel wrote into a row's spare columns"
     assert (s, o) == rng
     ref_out, ref_lse = sdpa_ref.fwd(q, k, v, p, causal, scale, *rng, bias=bias)
     ref_dq, ref_dk, ref_dv = sdpa_ref.bwd(do, q, k, v, p, causal, *rng, scale, bias=bias)
