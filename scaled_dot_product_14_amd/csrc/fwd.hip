@@ -485,6 +485,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
     l_run = l_new;
     m_run = m_new;
   } else if constexpr (NS > 1) {
+    // A lane's 16 values of a block go out as four 16-byte writes.
     float* cmb = reinterpret_cast<float*>(lds);
     constexpr int SLOT = (NEB * 16 + 2) * 64;
     if (ksp > 0) {
@@ -492,7 +493,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(eb * 16 + r) * 64 + lane] = oacc[eb][r];
+        for (int cg = 0; cg < 4; ++cg) {
+          f32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = oacc[eb][4 * cg + t];
+          reinterpret_cast<f32x4*>(dst)[(eb * 4 + cg) * 64 + lane] = v;
+        }
       dst[(NEB * 16) * 64 + lane] = m_run;
       dst[(NEB * 16 + 1) * 64 + lane] = l_run;
     }
@@ -510,8 +516,12 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
 #pragma unroll
         for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            oacc[eb][r] = oacc[eb][r] * a_s + src[(eb * 16 + r) * 64 + lane] * a_o;
+          for (int cg = 0; cg < 4; ++cg) {
+            const f32x4 v = reinterpret_cast<const f32x4*>(src)[(eb * 4 + cg) * 64 + lane];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              oacc[eb][4 * cg + t] = oacc[eb][4 * cg + t] * a_s + v[t] * a_o;
+          }
         l_run = l_run * a_s + l_o * a_o;
         m_run = m_new;
       }
