@@ -819,7 +819,13 @@ __device__ __forceinline__ void role_dq(const BwdParams& p, int bh, int qblk, un
 // first).  Entry s: bit 15 set for a dQ block, low bits the block's rank.
 constexpr int kMaxOrder = 1024;
 struct BwdOrder {
-  uint16_t item[kMaxOrder];
+  uint32_t word[kMaxOrder / 2];  // two entries a word, entry 2*i in the low half
+  void set(int s, uint16_t v) {
+    uint32_t& w = word[s >> 1];
+    w = (w & (0xFFFF0000u >> (16 * (s & 1)))) | ((uint32_t)v << (16 * (s & 1)));
+  }
+  // Read as a whole word: a scalar load, where a 16-bit read is a vector one.
+  __device__ int get(int s) const { return (int)(word[s >> 1] >> (16 * (s & 1))) & 0xFFFF; }
 };
 
 // Workgroup order: per head, blocks in BwdOrder order (or, past kMaxOrder
@@ -839,9 +845,11 @@ constexpr int bwd_lds_bytes() {
 
 template <int E, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16, bool KEEP, bool DBIAS,
           int ROLES = 3>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb, BwdOrder ord,
-                                                  int order) {
+__global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb, int order,
+                                                  BwdOrder ord) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[bwd_lds_bytes<E, BIAS, KEEP, ROLES>()];
+  // The parameters, the launch's ints and the table's first entries.
+  warm_kernargs<8 * 64>();
   const int bh_count = p.B * p.H;
   int bh, slot;
   if ((bh_count & 7) == 0) {
@@ -856,7 +864,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdParams p, int nkb, int nqb,
   bool dkdv;
   int rank;
   if (order == 1) {
-    const int e = ord.item[slot];
+    const int e = ord.get(slot);
     dkdv = (e & 0x8000) == 0;
     rank = e & 0x7FFF;
   } else if (order >= 2) {
@@ -891,6 +899,7 @@ template <int E, bool F16>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p, uint32_t nblk,
                                                         uint32_t total) {
   constexpr int CPR = E / 8, RPB = 256 / CPR;
+  warm_kernargs<sizeof(BwdParams) + 2 * sizeof(uint32_t)>();
   const int tid = threadIdx.x;
   const int col = tid % CPR;
   const float log2_scale = __log2f(p.scale);
@@ -957,7 +966,7 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, const Ti
       split = slots > 0 && (long)std::min(nkb, nqb) * bhn >= (E == 64 ? 8 : 2) * slots;
     }
   }
-  BwdOrder ord, ordk, ordq;
+  BwdOrder ord{}, ordk{}, ordq{};
   // Past kMaxOrder blocks (or when asked to) the blocks go out in an order the
   // kernel computes from the block index instead of the table.
   const bool table = tiles.bwd_order != 1;
@@ -987,9 +996,9 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, const Ti
                      [](const Item& a, const Item& b) { return a.cost > b.cost; });
     int n = 0, nk = 0, nq = 0;
     for (const Item& it : items) {
-      if (use_order) ord.item[n++] = (uint16_t)it.key;
-      if (use_k && (it.key & 0x8000) == 0) ordk.item[nk++] = (uint16_t)it.key;
-      if (use_q && (it.key & 0x8000) != 0) ordq.item[nq++] = (uint16_t)it.key;
+      if (use_order) ord.set(n++, (uint16_t)it.key);
+      if (use_k && (it.key & 0x8000) == 0) ordk.set(nk++, (uint16_t)it.key);
+      if (use_q && (it.key & 0x8000) != 0) ordq.set(nq++, (uint16_t)it.key);
     }
   }
   auto go3 = [&](auto c, auto d, auto bias, auto keep, auto db) {
@@ -998,15 +1007,15 @@ hipError_t launch_main_t(const BwdParams& p, bool causal, bool dropout, const Ti
     if constexpr (bwd_can_split<E, Df, Bf>()) {
       if (split) {
         hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>), dim3((unsigned)nkb * bhn),
-                           dim3(256), 0, stream, p, nkb, nqb, ordk, use_k ? 1 : 2);
+                           dim3(256), 0, stream, p, nkb, nqb, use_k ? 1 : 2, ordk);
         hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 2>), dim3((unsigned)nqb * bhn),
-                           dim3(256), 0, stream, p, nkb, nqb, ordq, use_q ? 1 : 3);
+                           dim3(256), 0, stream, p, nkb, nqb, use_q ? 1 : 3, ordq);
         return;
       }
     }
     hipLaunchKernelGGL((bwd_kernel<E, Cf, Df, Bf, F16, Kf, DBf, 3>),
-                       dim3((unsigned)(nkb + nqb) * bhn), dim3(256), 0, stream, p, nkb, nqb, ord,
-                       use_order);
+                       dim3((unsigned)(nkb + nqb) * bhn), dim3(256), 0, stream, p, nkb, nqb,
+                       use_order, ord);
   };
   auto go2 = [&](auto c, auto d, auto bias, auto keep) {
     if constexpr (decltype(bias)::value) {

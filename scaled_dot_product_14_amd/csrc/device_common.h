@@ -32,6 +32,24 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Reads one dword of every 64-byte line of the first BYTES bytes of the
+// kernel's arguments (at most eight lines), as one batch of scalar loads with
+// a single wait.  The argument loads the code issues afterwards then hit the
+// scalar cache; left alone they come in rounds (the tile's coordinates first,
+// then the pointers and strides the tile needs), each a memory round trip at
+// a kernel's start.
+template <int BYTES>
+__device__ __forceinline__ void warm_kernargs() {
+  static_assert(BYTES > 0 && BYTES <= 8 * 64, "one to eight lines");
+  const uint32_t __attribute__((address_space(4)))* ka =
+      (const uint32_t __attribute__((address_space(4)))*)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = i * 64 < BYTES ? ka[i * 16] : 0u;
+  asm volatile("" ::"s"(x[0]), "s"(x[1]), "s"(x[2]), "s"(x[3]), "s"(x[4]), "s"(x[5]), "s"(x[6]),
+               "s"(x[7]));
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -45,6 +45,8 @@
 // causal tile then waits a little before its first loads (longer the fewer
 // steps it has), so that the heaviest tiles, which set the kernel's length,
 // are served first.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_ring.h"
@@ -558,6 +560,7 @@ template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, b
 __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qtiles, int hold) {
   using G = FwdGeom<E, NQ, NS, BN, BIAS>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS_BYTES];
+  warm_kernargs<sizeof(FwdParams) + 2 * sizeof(int)>();
   int bh, rank;
   wg_to_tile(blockIdx.x, p.B * p.H, bh, rank);
   const int qt = CAUSAL ? (n_qtiles - 1 - rank) : rank;
@@ -571,11 +574,20 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 // workgroups of two sub-tiles x two shares of 64-key tiles.  Both kinds use 64
 // KB of LDS, so two workgroups share a compute unit whatever their kind, and
 // the longest chain of steps of a head is cut where it starts to dominate.
-// Workgroups 0 .. n_heavy*B*H-1 are the 32-row tiles, heaviest first; the
-// 64-row tiles follow, heaviest first; each kind keeps a head on one XCD.
+// Without a dispatch table, workgroups 0 .. n_heavy*B*H-1 are the 32-row
+// tiles, heaviest first, and the 64-row tiles follow, heaviest first; each
+// kind keeps a head on one XCD.
+constexpr int kSplitSlots = 64;
+struct SplitOrder {
+  // Tile of workgroup 8*s + x, for XCD x: bit 15 set for the 32-row kind,
+  // bits 8..14 the head among the XCD's B*H/8, bits 0..7 the rank in its kind.
+  uint32_t slot[kSplitSlots / 2];  // two 16-bit entries a word, slot 2*i in the low half
+  int n;                           // slots in use; 0 when there is no table
+};
+
 template <int E, bool DROPOUT, bool BIAS, bool F16>
 __global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy, int n_light,
-                                                        int hold) {
+                                                        int hold, SplitOrder ord) {
   using GH = FwdGeom<E, 1, 4, 32, BIAS>;
   using GL = FwdGeom<E, 2, 2, 64, BIAS>;
   constexpr int LDS_B = GH::LDS_BYTES > GL::LDS_BYTES ? GH::LDS_BYTES : GL::LDS_BYTES;
@@ -584,13 +596,23 @@ __global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy
   const int light_rows = n_light * 64;
   const int nh = n_heavy * bh_count;
   int bh, rank;
-  if ((int)blockIdx.x < nh) {
-    wg_to_tile(blockIdx.x, bh_count, bh, rank);
+  bool heavy;
+  warm_kernargs<sizeof(FwdParams) + 3 * sizeof(int) + sizeof(SplitOrder)>();
+  if (ord.n > 0) {
+    const int s = blockIdx.x >> 3;
+    const int code = (ord.slot[s >> 1] >> (16 * (s & 1))) & 0xFFFF;
+    heavy = (code & 0x8000) != 0;
+    bh = (int)(blockIdx.x & 7) * (bh_count >> 3) + ((code >> 8) & 127);
+    rank = code & 255;
+  } else {
+    heavy = (int)blockIdx.x < nh;
+    wg_to_tile(heavy ? (int)blockIdx.x : (int)blockIdx.x - nh, bh_count, bh, rank);
+  }
+  if (heavy) {
     const int qt = light_rows / 32 + (n_heavy - 1 - rank);
     fwd_tile<E, 1, 4, 32, true, DROPOUT, BIAS, F16, 1>(
         p, bh, qt, causal_steps_max(p, light_rows + 32 * n_heavy, 32, 4), hold, lds);
   } else {
-    wg_to_tile((int)blockIdx.x - nh, bh_count, bh, rank);
     const int qt = n_light - 1 - rank;
     fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, causal_steps_max(p, light_rows, 64, 2),
                                                     hold, lds);
@@ -649,6 +671,55 @@ inline SplitRows split_rows(int Sq) {
   return {light_rows / 64, (Sq - light_rows + 31) / 32};
 }
 
+// Dispatch table that pairs long tiles with short ones on a compute unit when
+// the whole grid is resident.  The dispatcher deals workgroups to the XCDs in
+// turn (workgroup w to XCD w % 8) and, within an XCD, gives every compute unit
+// one workgroup before any gets a second, so the XCD's slots s and s + C
+// (C compute units per XCD) share a unit.  The tiles of the XCD's heads are
+// sorted by an estimate of their length (steps times the cost of a step of
+// their kind); the longest run alone in the slots the second round leaves
+// empty, and the rest pair longest with shortest.  Placement only moves time
+// around: each tile computes the same values wherever it runs.
+SplitOrder split_order(const FwdParams& p, const SplitRows& r) {
+  SplitOrder o{};
+  const int bh_count = p.B * p.H, cus = device_cus();
+  if (bh_count % 8 != 0 || cus % 8 != 0) return o;
+  const int per_xcd = bh_count / 8, C = cus / 8;
+  const int n = per_xcd * (r.n_light + r.n_heavy);
+  if (n > 2 * C || n > kSplitSlots || per_xcd > 128 || r.n_light > 256 || r.n_heavy > 256) return o;
+  auto steps = [&](int rows, int bn, int ns) {
+    const int kend = std::min(p.Sk, std::min(p.Sq, rows));
+    return ((kend + bn - 1) / bn + ns - 1) / ns;
+  };
+  struct Item {
+    int cost;
+    uint16_t code;
+  };
+  Item items[kSplitSlots];
+  int k = 0;
+  for (int j = 0; j < per_xcd; ++j) {
+    for (int rank = 0; rank < r.n_heavy; ++rank) {
+      const int qt = r.n_light * 2 + r.n_heavy - 1 - rank;  // in 32-row tiles
+      items[k++] = {3 * steps((qt + 1) * 32, 32, 4), (uint16_t)(0x8000 | j << 8 | rank)};
+    }
+    for (int rank = 0; rank < r.n_light; ++rank) {
+      const int qt = r.n_light - 1 - rank;
+      items[k++] = {5 * steps((qt + 1) * 64, 64, 2), (uint16_t)(j << 8 | rank)};
+    }
+  }
+  std::stable_sort(items, items + n, [](const Item& a, const Item& b) { return a.cost > b.cost; });
+  const int m = std::max(n - C, 0);            // compute units that get two tiles
+  const int alone = std::min(n, C) - m;        // compute units that get one
+  auto put = [&](int s, uint16_t code) { o.slot[s >> 1] |= (uint32_t)code << (16 * (s & 1)); };
+  for (int j = 0; j < m; ++j) {
+    put(j, items[alone + j].code);          // longest of the paired ...
+    put(C + j, items[n - 1 - j].code);      // ... with the shortest
+  }
+  for (int t = 0; t < alone; ++t) put(m + t, items[t].code);
+  o.n = n;
+  return o;
+}
+
 template <int E>
 hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, hipStream_t stream) {
   const SplitRows r = split_rows(p.Sq);
@@ -657,8 +728,10 @@ hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, hipStrea
     constexpr auto kernel = &fwd_split_kernel<E, decltype(d)::value, decltype(bias)::value,
                                               decltype(half)::value>;
     const long slots = (long)device_cus() * resident_per_cu<kernel>(256);
-    const int hold = ((long)grid.x <= slots) ? kHoldSteps : 0;
-    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light, hold);
+    const bool resident = (long)grid.x <= slots;
+    const SplitOrder ord = resident ? split_order(p, r) : SplitOrder{};
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light,
+                       resident ? kHoldSteps : 0, ord);
   };
   auto with_half = [&](auto d, auto bias) {
     if (f16)

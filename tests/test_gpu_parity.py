@@ -127,6 +127,12 @@ EXTRA = [
     # Sq > Sk and ragged lengths, several heads and batches.
     (2, 3, 257, 200, 128, "BSHE", True, 0.0, 22),
     (1, 2, 190, 700, 128, "BHSE", False, 0.0, 23),
+    # The causal split forward with its dispatch table (B*H a multiple of 8,
+    # the whole grid resident): tiles paired on compute units (16 heads of
+    # 1000 ragged rows, dropout), and every tile alone (8 heads, head dim 40,
+    # Sq < Sk, BSHE).
+    (2, 8, 1000, 1000, 64, "BHSE", True, 0.1, 24),
+    (1, 8, 700, 900, 40, "BSHE", True, 0.0, 25),
 ]
 
 
