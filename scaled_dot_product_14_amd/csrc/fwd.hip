@@ -155,7 +155,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
   const int n_it = (n_kt + NS - 1) / NS;
 
   // Start-up hold: up to `hold` sleeps of ~640 clocks, one per step this tile
-  // has fewer than the heaviest one.
+  // has fewer than the heaviest one (the split launch's dispatch table gives
+  // the count itself, with n_it_max out of reach).
   if (CAUSAL && hold > 0) {
     const int units = min(n_it_max - n_it, hold);
     for (int i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(10);
@@ -580,7 +581,8 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 constexpr int kSplitSlots = 64;
 struct SplitOrder {
   // Tile of workgroup 8*s + x, for XCD x: bit 15 set for the 32-row kind,
-  // bits 8..14 the head among the XCD's B*H/8, bits 0..7 the rank in its kind.
+  // bits 12..14 its start-up hold in sleep units, bits 6..11 the head among
+  // the XCD's B*H/8, bits 0..5 the rank in its kind.
   uint32_t slot[kSplitSlots / 2];  // two 16-bit entries a word, slot 2*i in the low half
   int n;                           // slots in use; 0 when there is no table
 };
@@ -598,24 +600,28 @@ __global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy
   int bh, rank;
   bool heavy;
   warm_kernargs<sizeof(FwdParams) + 3 * sizeof(int) + sizeof(SplitOrder)>();
+  // With a table the hold comes from it: n_it_max past any tile's steps makes
+  // the hold's count the table's.
+  int nmax_h = causal_steps_max(p, light_rows + 32 * n_heavy, 32, 4);
+  int nmax_l = causal_steps_max(p, light_rows, 64, 2);
   if (ord.n > 0) {
     const int s = blockIdx.x >> 3;
     const int code = (ord.slot[s >> 1] >> (16 * (s & 1))) & 0xFFFF;
     heavy = (code & 0x8000) != 0;
-    bh = (int)(blockIdx.x & 7) * (bh_count >> 3) + ((code >> 8) & 127);
-    rank = code & 255;
+    hold = (code >> 12) & 7;
+    nmax_h = nmax_l = 1 << 20;
+    bh = (int)(blockIdx.x & 7) * (bh_count >> 3) + ((code >> 6) & 63);
+    rank = code & 63;
   } else {
     heavy = (int)blockIdx.x < nh;
     wg_to_tile(heavy ? (int)blockIdx.x : (int)blockIdx.x - nh, bh_count, bh, rank);
   }
   if (heavy) {
     const int qt = light_rows / 32 + (n_heavy - 1 - rank);
-    fwd_tile<E, 1, 4, 32, true, DROPOUT, BIAS, F16, 1>(
-        p, bh, qt, causal_steps_max(p, light_rows + 32 * n_heavy, 32, 4), hold, lds);
+    fwd_tile<E, 1, 4, 32, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, nmax_h, hold, lds);
   } else {
     const int qt = n_light - 1 - rank;
-    fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, causal_steps_max(p, light_rows, 64, 2),
-                                                    hold, lds);
+    fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, nmax_l, hold, lds);
   }
 }
 
@@ -686,7 +692,7 @@ SplitOrder split_order(const FwdParams& p, const SplitRows& r) {
   if (bh_count % 8 != 0 || cus % 8 != 0) return o;
   const int per_xcd = bh_count / 8, C = cus / 8;
   const int n = per_xcd * (r.n_light + r.n_heavy);
-  if (n > 2 * C || n > kSplitSlots || per_xcd > 128 || r.n_light > 256 || r.n_heavy > 256) return o;
+  if (n > 2 * C || n > kSplitSlots || per_xcd > 64 || r.n_light > 64 || r.n_heavy > 64) return o;
   auto steps = [&](int rows, int bn, int ns) {
     const int kend = std::min(p.Sk, std::min(p.Sq, rows));
     return ((kend + bn - 1) / bn + ns - 1) / ns;
@@ -700,22 +706,29 @@ SplitOrder split_order(const FwdParams& p, const SplitRows& r) {
   for (int j = 0; j < per_xcd; ++j) {
     for (int rank = 0; rank < r.n_heavy; ++rank) {
       const int qt = r.n_light * 2 + r.n_heavy - 1 - rank;  // in 32-row tiles
-      items[k++] = {3 * steps((qt + 1) * 32, 32, 4), (uint16_t)(0x8000 | j << 8 | rank)};
+      items[k++] = {3 * steps((qt + 1) * 32, 32, 4), (uint16_t)(0x8000 | j << 6 | rank)};
     }
     for (int rank = 0; rank < r.n_light; ++rank) {
       const int qt = r.n_light - 1 - rank;
-      items[k++] = {5 * steps((qt + 1) * 64, 64, 2), (uint16_t)(j << 8 | rank)};
+      items[k++] = {5 * steps((qt + 1) * 64, 64, 2), (uint16_t)(j << 6 | rank)};
     }
   }
   std::stable_sort(items, items + n, [](const Item& a, const Item& b) { return a.cost > b.cost; });
   const int m = std::max(n - C, 0);            // compute units that get two tiles
   const int alone = std::min(n, C) - m;        // compute units that get one
-  auto put = [&](int s, uint16_t code) { o.slot[s >> 1] |= (uint32_t)code << (16 * (s & 1)); };
+  auto put = [&](int s, uint16_t code, int hold) {
+    o.slot[s >> 1] |= (uint32_t)(code | hold << 12) << (16 * (s & 1));
+  };
+  // The shorter tile of a pair holds back one sleep unit (~0.3 us) per
+  // 32-row step (3 cost units) of estimated length it has less than its
+  // partner; the longer one and the tiles alone start at once.
   for (int j = 0; j < m; ++j) {
-    put(j, items[alone + j].code);          // longest of the paired ...
-    put(C + j, items[n - 1 - j].code);      // ... with the shortest
+    const Item& a = items[alone + j];  // longest of the paired ...
+    const Item& b = items[n - 1 - j];  // ... with the shortest
+    put(j, a.code, 0);
+    put(C + j, b.code, std::min(kHoldSteps, (a.cost - b.cost) / 3));
   }
-  for (int t = 0; t < alone; ++t) put(m + t, items[t].code);
+  for (int t = 0; t < alone; ++t) put(m + t, items[t].code, 0);
   o.n = n;
   return o;
 }
