@@ -136,6 +136,19 @@ EXTRA = [
 ]
 
 
+@pytest.mark.parametrize("B,H,S,p,heads,seed", [
+    # Long causal heads, whose split launch gives about the last quarter of
+    # the rows to the 32-row kind: with the dispatch table (8 heads of 2200
+    # rows, a 576-row tail, tiles paired on compute units) and without it (6
+    # heads, dropout; two heads against the oracle).
+    (1, 8, 2200, 0.0, None, 26),
+    (1, 6, 1536, 0.1, [(0, 0), (0, 5)], 27),
+])
+def test_long_causal_split(B, H, S, p, heads, seed):
+    q, k, v, do = workloads.draw(B, H, S, S, 64, seed, 1.0, "BHSE", device="cuda")
+    check_full(f"long{seed}", q, k, v, do, p, True, (seed * 1000 + 7, seed * 13), heads=heads)
+
+
 @pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,p,seed", EXTRA)
 def test_extra_cases(B, H, Sq, Sk, E, layout, causal, p, seed):
     q, k, v, do = workloads.draw(B, H, Sq, Sk, E, seed, 1.0, layout, device="cuda")
