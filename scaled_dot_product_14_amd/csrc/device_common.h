@@ -38,8 +38,10 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
 // scalar cache; left alone they come in rounds (the tile's coordinates first,
 // then the pointers and strides the tile needs), each a memory round trip at
 // a kernel's start.
+// `also` joins the batch: an argument the caller reads at an index of its
+// own (a table entry picked by the workgroup index) costs no extra round trip.
 template <int BYTES>
-__device__ __forceinline__ void warm_kernargs() {
+__device__ __forceinline__ void warm_kernargs(uint32_t also = 0u) {
   static_assert(BYTES > 0 && BYTES <= 8 * 64, "one to eight lines");
   const uint32_t __attribute__((address_space(4)))* ka =
       (const uint32_t __attribute__((address_space(4)))*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -47,7 +49,7 @@ __device__ __forceinline__ void warm_kernargs() {
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = i * 64 < BYTES ? ka[i * 16] : 0u;
   asm volatile("" ::"s"(x[0]), "s"(x[1]), "s"(x[2]), "s"(x[3]), "s"(x[4]), "s"(x[5]), "s"(x[6]),
-               "s"(x[7]));
+               "s"(x[7]), "s"(also));
 }
 
 __device__ __forceinline__ f32x16 zero16() {

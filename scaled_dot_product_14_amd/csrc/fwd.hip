@@ -46,6 +46,7 @@
 // steps it has), so that the heaviest tiles, which set the kernel's length,
 // are served first.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -578,40 +579,71 @@ __global__ __launch_bounds__(NQ* NS * 64) void fwd_kernel(FwdParams p, int n_qti
 // Without a dispatch table, workgroups 0 .. n_heavy*B*H-1 are the 32-row
 // tiles, heaviest first, and the 64-row tiles follow, heaviest first; each
 // kind keeps a head on one XCD.
-constexpr int kSplitSlots = 64;
-struct SplitOrder {
-  // Tile of workgroup 8*s + x, for XCD x: bit 15 set for the 32-row kind,
-  // bits 12..14 its start-up hold in sleep units, bits 6..11 the head among
-  // the XCD's B*H/8, bits 0..5 the rank in its kind.
-  uint32_t slot[kSplitSlots / 2];  // two 16-bit entries a word, slot 2*i in the low half
-  int n;                           // slots in use; 0 when there is no table
+//
+// A dispatch table (below) can instead name each workgroup's tile, in one of
+// two forms, each its own kernel so that the smaller one keeps the kernel
+// arguments short (a longer argument block measured 1-3% slower per launch).
+// With B*H a multiple of 8, SplitOrderXcd: every XCD has the same number of
+// heads, and one 64-entry table, indexed by the workgroup's slot in its XCD,
+// serves them all.
+constexpr int kXcdSlots = 64;
+struct SplitOrderXcd {
+  int n;  // workgroups the table covers; 0 when there is none
+  // Tile of workgroup 8*s + x, for XCD x, 16 bits, two to a word (s even in
+  // the low half): bit 15 set for the 32-row kind, bits 12..14 its start-up
+  // hold in sleep units, bits 6..11 its head among the XCD's B*H/8, bits 0..5
+  // its rank in its kind.
+  uint32_t slot[kXcdSlots / 2];
+};
+// Otherwise SplitOrderAll, one entry per workgroup.
+constexpr int kSplitSlots = 512;
+struct SplitOrderAll {
+  int n;
+  // Tile of workgroup w: bit 31 set for the 32-row kind, bits 28..30 its
+  // start-up hold, bits 12..27 its (batch, head) index b*H + h, bits 0..11 its
+  // rank in its kind.
+  uint32_t slot[kSplitSlots];
 };
 
-template <int E, bool DROPOUT, bool BIAS, bool F16>
+template <int E, bool DROPOUT, bool BIAS, bool F16, typename ORD>
 __global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy, int n_light,
-                                                        int hold, SplitOrder ord) {
+                                                        int hold, ORD ord) {
   using GH = FwdGeom<E, 1, 4, 32, BIAS>;
   using GL = FwdGeom<E, 2, 2, 64, BIAS>;
   constexpr int LDS_B = GH::LDS_BYTES > GL::LDS_BYTES ? GH::LDS_BYTES : GL::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_B];
+  constexpr bool ALL = std::is_same<ORD, SplitOrderAll>::value;
+  constexpr int ARG_B = (int)(sizeof(FwdParams) + 3 * sizeof(int) + sizeof(ORD));
+  // The workgroup's table word is read in the same batch as the warm-up.
+  uint32_t word;
+  if constexpr (ALL)
+    word = ord.slot[min((int)blockIdx.x, kSplitSlots - 1)];
+  else
+    word = ord.slot[min((int)blockIdx.x >> 4, kXcdSlots / 2 - 1)];
+  warm_kernargs<(ARG_B < 8 * 64 ? ARG_B : 8 * 64)>(word);
   const int bh_count = p.B * p.H;
   const int light_rows = n_light * 64;
   const int nh = n_heavy * bh_count;
   int bh, rank;
   bool heavy;
-  warm_kernargs<sizeof(FwdParams) + 3 * sizeof(int) + sizeof(SplitOrder)>();
   // With a table the hold comes from it: n_it_max past any tile's steps makes
   // the hold's count the table's.
   int nmax_h = causal_steps_max(p, light_rows + 32 * n_heavy, 32, 4);
   int nmax_l = causal_steps_max(p, light_rows, 64, 2);
   if (ord.n > 0) {
-    const int s = blockIdx.x >> 3;
-    const int code = (ord.slot[s >> 1] >> (16 * (s & 1))) & 0xFFFF;
-    heavy = (code & 0x8000) != 0;
-    hold = (code >> 12) & 7;
     nmax_h = nmax_l = 1 << 20;
-    bh = (int)(blockIdx.x & 7) * (bh_count >> 3) + ((code >> 6) & 63);
-    rank = code & 63;
+    if constexpr (ALL) {
+      heavy = (word >> 31) != 0;
+      hold = (int)((word >> 28) & 7);
+      bh = (int)((word >> 12) & 0xFFFF);
+      rank = (int)(word & 0xFFF);
+    } else {
+      const uint32_t code = (word >> (16 * ((blockIdx.x >> 3) & 1))) & 0xFFFF;
+      heavy = (code >> 15) != 0;
+      hold = (int)((code >> 12) & 7);
+      bh = (int)(blockIdx.x & 7) * (bh_count >> 3) + (int)((code >> 6) & 63);
+      rank = (int)(code & 63);
+    }
   } else {
     heavy = (int)blockIdx.x < nh;
     wg_to_tile(heavy ? (int)blockIdx.x : (int)blockIdx.x - nh, bh_count, bh, rank);
@@ -694,56 +726,142 @@ inline SplitRows split_rows(const FwdParams& p) {
 // the whole grid is resident.  The dispatcher deals workgroups to the XCDs in
 // turn (workgroup w to XCD w % 8) and, within an XCD, gives every compute unit
 // one workgroup before any gets a second, so the XCD's slots s and s + C
-// (C compute units per XCD) share a unit.  The tiles of the XCD's heads are
-// sorted by an estimate of their length (steps times the cost of a step of
-// their kind); the longest run alone in the slots the second round leaves
-// empty, and the rest pair longest with shortest.  Placement only moves time
-// around: each tile computes the same values wherever it runs.
-SplitOrder split_order(const FwdParams& p, const SplitRows& r) {
-  SplitOrder o{};
+// (workgroups 8s + x and 8(s + C) + x, C compute units per XCD) share a unit.
+// Tiles are costed as steps times the cost of a step of their kind.  With B*H
+// a multiple of 8 each XCD takes B*H/8 whole heads, so their K and V stay in
+// its L2; otherwise the tiles go out longest first to the XCD with the least
+// work so far (plus a penalty for a head it does not hold yet) that has room.
+// Within an XCD the longest tiles run alone in the slots the second round
+// leaves empty, and the rest pair longest with shortest.  Placement only moves
+// time around: each tile computes the same values wherever it runs.
+struct SplitPlan {
+  int n;  // workgroups planned; 0: no table
+  struct Tile {
+    bool heavy;
+    int hold, bh, rank;
+  } tile[kSplitSlots];  // by workgroup
+};
+
+void plan_split(const FwdParams& p, const SplitRows& r, SplitPlan& plan) {
+  plan.n = 0;
   const int bh_count = p.B * p.H, cus = device_cus();
-  if (bh_count % 8 != 0 || cus % 8 != 0) return o;
-  const int per_xcd = bh_count / 8, C = cus / 8;
-  const int n = per_xcd * (r.n_light + r.n_heavy);
-  if (n > 2 * C || n > kSplitSlots || per_xcd > 64 || r.n_light > 64 || r.n_heavy > 64) return o;
+  // Fewer than 8 heads would spread each head over several XCDs: measured
+  // slower than the default order there.
+  if (cus % 8 != 0 || bh_count < 8) return;
+  const int C = cus / 8;
+  const long nl = (long)bh_count * (r.n_light + r.n_heavy);
+  if (nl > 2L * cus || nl > kSplitSlots) return;
+  const int n = (int)nl;
   auto steps = [&](int rows, int bn, int ns) {
     const int kend = std::min(p.Sk, std::min(p.Sq, rows));
     return ((kend + bn - 1) / bn + ns - 1) / ns;
   };
   struct Item {
-    int cost;
-    uint16_t code;
+    int cost, bh, rank;
+    bool heavy;
   };
-  Item items[kSplitSlots];
+  auto longer = [](const Item& a, const Item& b) { return a.cost > b.cost; };
+  static thread_local Item items[kSplitSlots], by_xcd[8][kSplitSlots / 8 + 1];
   int k = 0;
-  for (int j = 0; j < per_xcd; ++j) {
+  for (int bh = 0; bh < bh_count; ++bh) {
     for (int rank = 0; rank < r.n_heavy; ++rank) {
       const int qt = r.n_light * 2 + r.n_heavy - 1 - rank;  // in 32-row tiles
-      items[k++] = {3 * steps((qt + 1) * 32, 32, 4), (uint16_t)(0x8000 | j << 6 | rank)};
+      items[k++] = {3 * steps((qt + 1) * 32, 32, 4), bh, rank, true};
     }
     for (int rank = 0; rank < r.n_light; ++rank) {
       const int qt = r.n_light - 1 - rank;
-      items[k++] = {5 * steps((qt + 1) * 64, 64, 2), (uint16_t)(j << 6 | rank)};
+      items[k++] = {5 * steps((qt + 1) * 64, 64, 2), bh, rank, false};
     }
   }
-  std::stable_sort(items, items + n, [](const Item& a, const Item& b) { return a.cost > b.cost; });
-  const int m = std::max(n - C, 0);            // compute units that get two tiles
-  const int alone = std::min(n, C) - m;        // compute units that get one
-  auto put = [&](int s, uint16_t code, int hold) {
-    o.slot[s >> 1] |= (uint32_t)(code | hold << 12) << (16 * (s & 1));
-  };
-  // The shorter tile of a pair holds back one sleep unit (~0.3 us) per
-  // 32-row step (3 cost units) of estimated length it has less than its
-  // partner; the longer one and the tiles alone start at once.
-  for (int j = 0; j < m; ++j) {
-    const Item& a = items[alone + j];  // longest of the paired ...
-    const Item& b = items[n - 1 - j];  // ... with the shortest
-    put(j, a.code, 0);
-    put(C + j, b.code, std::min(kHoldSteps, (a.cost - b.cost) / 3));
+  int cnt[8] = {0};
+  if (bh_count % 8 == 0) {
+    const int per = bh_count / 8;
+    for (int i = 0; i < n; ++i) {
+      const int x = items[i].bh / per;
+      by_xcd[x][cnt[x]++] = items[i];
+    }
+  } else {
+    std::stable_sort(items, items + n, longer);
+    long load[8] = {0}, total = 0;
+    for (int i = 0; i < n; ++i) total += items[i].cost;
+    const long penalty = 2 * total / n;  // two average tiles
+    static thread_local unsigned char holds[8][kSplitSlots];  // XCD x has tiles of head bh
+    for (int x = 0; x < 8; ++x) std::fill(holds[x], holds[x] + bh_count, 0);
+    for (int i = 0; i < n; ++i) {
+      const Item& it = items[i];
+      int best = -1;
+      long best_score = 0;
+      for (int x = 0; x < 8; ++x) {
+        if (cnt[x] >= (n - x + 7) / 8) continue;  // XCD x runs (n - x + 7) / 8 workgroups
+        const long score = load[x] + (holds[x][it.bh] ? 0 : penalty);
+        if (best < 0 || score < best_score) best = x, best_score = score;
+      }
+      by_xcd[best][cnt[best]++] = it;
+      load[best] += it.cost;
+      holds[best][it.bh] = 1;
+    }
   }
-  for (int t = 0; t < alone; ++t) put(m + t, items[t].code, 0);
-  o.n = n;
-  return o;
+  for (int x = 0; x < 8; ++x) {
+    Item* v = by_xcd[x];
+    const int nx = cnt[x];
+    std::stable_sort(v, v + nx, longer);
+    const int m = std::max(nx - C, 0);      // compute units that get two tiles
+    const int alone = std::min(nx, C) - m;  // compute units that get one
+    auto put = [&](int s, const Item& it, int hold) {
+      plan.tile[8 * s + x] = {it.heavy, hold, it.bh, it.rank};
+    };
+    // The shorter tile of a pair holds back one sleep unit (~0.3 us) per
+    // 32-row step (3 cost units) of estimated length it has less than its
+    // partner; the longer one and the tiles alone start at once.
+    for (int j = 0; j < m; ++j) {
+      const Item& a = v[alone + j];   // longest of the paired ...
+      const Item& b = v[nx - 1 - j];  // ... with the shortest
+      put(j, a, 0);
+      put(C + j, b, std::min(kHoldSteps, (a.cost - b.cost) / 3));
+    }
+    for (int t = 0; t < alone; ++t) put(m + t, v[t], 0);
+  }
+  plan.n = n;
+}
+
+// The plan and its two encodings for the last shape seen on this thread.
+struct SplitTables {
+  int key[7];
+  SplitPlan plan;
+  SplitOrderXcd xcd;
+  SplitOrderAll all;
+};
+
+const SplitTables& split_tables(const FwdParams& p, const SplitRows& r) {
+  static thread_local SplitTables t{{-1, 0, 0, 0, 0, 0, 0}, {}, {}, {}};
+  const int key[7] = {p.B, p.H, p.Sq, p.Sk, r.n_light, r.n_heavy, device_cus()};
+  if (std::equal(key, key + 7, t.key)) return t;
+  std::copy(key, key + 7, t.key);
+  plan_split(p, r, t.plan);
+  t.xcd = SplitOrderXcd{};
+  t.all = SplitOrderAll{};
+  const int n = t.plan.n, bh_count = p.B * p.H;
+  if (n == 0) return t;
+  if (bh_count % 8 == 0 && n / 8 <= kXcdSlots) {
+    // Per-XCD form: entries of XCD 0 (the others hold the same pattern).
+    const int per = bh_count / 8;
+    for (int w = 0; w < n; w += 8) {
+      const SplitPlan::Tile& tl = t.plan.tile[w];
+      const int s = w / 8;
+      const uint32_t code = (tl.heavy ? 0x8000u : 0u) | (uint32_t)tl.hold << 12 |
+                            (uint32_t)(tl.bh % per) << 6 | (uint32_t)tl.rank;
+      t.xcd.slot[s >> 1] |= code << (16 * (s & 1));
+    }
+    t.xcd.n = n;
+  } else if (bh_count % 8 != 0) {
+    for (int w = 0; w < n; ++w) {
+      const SplitPlan::Tile& tl = t.plan.tile[w];
+      t.all.slot[w] = (tl.heavy ? 1u << 31 : 0u) | (uint32_t)tl.hold << 28 |
+                      (uint32_t)tl.bh << 12 | (uint32_t)tl.rank;
+    }
+    t.all.n = n;
+  }
+  return t;
 }
 
 template <int E>
@@ -751,13 +869,24 @@ hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, hipStrea
   const SplitRows r = split_rows(p);
   const dim3 grid((unsigned)(r.n_light + r.n_heavy) * (unsigned)(p.B * p.H));
   auto go = [&](auto d, auto bias, auto half) {
-    constexpr auto kernel = &fwd_split_kernel<E, decltype(d)::value, decltype(bias)::value,
-                                              decltype(half)::value>;
+    constexpr bool D = decltype(d)::value, Bi = decltype(bias)::value, H = decltype(half)::value;
+    constexpr auto kernel = &fwd_split_kernel<E, D, Bi, H, SplitOrderXcd>;
+    constexpr auto kernel_all = &fwd_split_kernel<E, D, Bi, H, SplitOrderAll>;
     const long slots = (long)device_cus() * resident_per_cu<kernel>(256);
     const bool resident = (long)grid.x <= slots;
-    const SplitOrder ord = resident ? split_order(p, r) : SplitOrder{};
-    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light,
-                       resident ? kHoldSteps : 0, ord);
+    const int hold = resident ? kHoldSteps : 0;
+    if (resident) {
+      const SplitTables& t = split_tables(p, r);
+      if (t.all.n > 0) {
+        hipLaunchKernelGGL(kernel_all, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light, hold,
+                           t.all);
+        return;
+      }
+      hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light, hold, t.xcd);
+      return;
+    }
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light, hold,
+                       SplitOrderXcd{});
   };
   auto with_half = [&](auto d, auto bias) {
     if (f16)

@@ -138,11 +138,16 @@ EXTRA = [
 
 @pytest.mark.parametrize("B,H,S,p,heads,seed", [
     # Long causal heads, whose split launch gives about the last quarter of
-    # the rows to the 32-row kind: with the dispatch table (8 heads of 2200
-    # rows, a 576-row tail, tiles paired on compute units) and without it (6
-    # heads, dropout; two heads against the oracle).
+    # the rows to the 32-row kind: with the per-XCD dispatch table (8 heads of
+    # 2200 rows, a 576-row tail, tiles paired on compute units) and without a
+    # table (6 heads, dropout; two heads against the oracle).
     (1, 8, 2200, 0.0, None, 26),
     (1, 6, 1536, 0.1, [(0, 0), (0, 5)], 27),
+    # B*H not a multiple of 8: the table with one entry per workgroup, heads
+    # dealt over the XCDs by estimated work (12 heads; 20 heads of ragged
+    # length with dropout).
+    (1, 12, 1536, 0.0, [(0, 0), (0, 5), (0, 11)], 28),
+    (2, 10, 1000, 0.1, [(0, 3), (1, 9)], 29),
 ])
 def test_long_causal_split(B, H, S, p, heads, seed):
     q, k, v, do = workloads.draw(B, H, S, S, 64, seed, 1.0, "BHSE", device="cuda")
