@@ -149,9 +149,32 @@ EXTRA = [
     (1, 12, 1536, 0.0, [(0, 0), (0, 5), (0, 11)], 28),
     (2, 10, 1000, 0.1, [(0, 3), (1, 9)], 29),
 ])
-def test_long_causal_split(B, H, S, p, heads, seed):
+def test_long_causal_split(B, H, S, p, heads, seed, monkeypatch):
     q, k, v, do = workloads.draw(B, H, S, S, 64, seed, 1.0, "BHSE", device="cuda")
-    check_full(f"long{seed}", q, k, v, do, p, True, (seed * 1000 + 7, seed * 13), heads=heads)
+    rng = (seed * 1000 + 7, seed * 13)
+    check_full(f"long{seed}", q, k, v, do, p, True, rng, heads=heads)
+    # Every head, not only those checked against the oracle: into NaN-filled
+    # outputs, each element must be written, and must match the two-by-two
+    # launch, which cuts the same rows into other tiles (same dropout mask).
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device="cuda")
+    sdpa.sdpa_set_rng_state(*rng)
+    sdpa.sdpa_fwd(q, k, v, p, True, None, out=out, lse=lse)
+    monkeypatch.setenv("SDPA14_FWD_SHAPE", "2")
+    sdpa.sdpa_set_rng_state(*rng)
+    out2, lse2, _, _ = sdpa.sdpa_fwd(q, k, v, p, True, None)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "output elements left unwritten"
+    assert torch.isfinite(lse).all().item(), "LSE rows left unwritten"
+    diff = (out.float() - out2.float()).abs()
+    d_lse = (lse - lse2).abs().max().item()
+    say(f"  split vs two-by-two, all heads: max |d out| {diff.max().item():.2e}, "
+        f"max |d lse| {d_lse:.2e}")
+    # Each launch is within the output bar (1e-2, or a rounding of the value
+    # where bf16 cannot reach it) and the LSE bar (1e-3) of the exact values,
+    # so they are within twice the bars, plus one bf16 ulp, of each other.
+    assert (diff <= 2e-2 + out2.float().abs() * 2.0 ** -7).all().item()
+    assert d_lse <= 2e-3
 
 
 @pytest.mark.parametrize("B,H,Sq,Sk,E,layout,causal,p,seed", EXTRA)
