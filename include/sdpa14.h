@@ -65,13 +65,15 @@
  * call return SDPA_ERR_HIP after validation and before any HIP call: nothing
  * is enqueued and the RNG state is untouched.
  *
- * Kernel choices are made per problem.  For comparing them, three variables,
+ * Kernel choices are made per problem.  For comparing them, four variables,
  * read on every call, force one (results are the same within the parity bars;
- * the backward's forms are bitwise the same): SDPA14_FWD_SHAPE (1: four
- * 32-row sub-tiles, 2: two sub-tiles x two key shares, 3: one sub-tile x four
- * key shares, 4: the causal split launch; a shape the problem cannot take
- * runs as 2), SDPA14_BWD_ROLES (1: the backward's two workgroup roles in one
- * launch, 2: in two; two need a call without dropout or bias) and
+ * the backward's forms and the two forward orders are bitwise the same):
+ * SDPA14_FWD_SHAPE (1: four 32-row sub-tiles, 2: two sub-tiles x two key
+ * shares, 3: one sub-tile x four key shares, 4: the causal split launch; a
+ * shape the problem cannot take runs as 2), SDPA14_FWD_ORDER (1: the causal
+ * split forward in its default workgroup order instead of the host-built
+ * dispatch table), SDPA14_BWD_ROLES (1: the backward's two workgroup roles in
+ * one launch, 2: in two; two need a call without dropout or bias) and
  * SDPA14_BWD_ORDER (1: the block order computed from the block index instead
  * of the host-built table).
  */

@@ -865,7 +865,8 @@ const SplitTables& split_tables(const FwdParams& p, const SplitRows& r) {
 }
 
 template <int E>
-hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, hipStream_t stream) {
+hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, bool table,
+                            hipStream_t stream) {
   const SplitRows r = split_rows(p);
   const dim3 grid((unsigned)(r.n_light + r.n_heavy) * (unsigned)(p.B * p.H));
   auto go = [&](auto d, auto bias, auto half) {
@@ -875,7 +876,7 @@ hipError_t launch_fwd_split(const FwdParams& p, bool dropout, bool f16, hipStrea
     const long slots = (long)device_cus() * resident_per_cu<kernel>(256);
     const bool resident = (long)grid.x <= slots;
     const int hold = resident ? kHoldSteps : 0;
-    if (resident) {
+    if (resident && table) {
       const SplitTables& t = split_tables(p, r);
       if (t.all.n > 0) {
         hipLaunchKernelGGL(kernel_all, grid, dim3(256), 0, stream, p, r.n_heavy, r.n_light, hold,
@@ -942,7 +943,7 @@ hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
       shape = 2;
   }
   if (shape == 4 && (E != 64 || !causal)) shape = 2;  // the split launch is causal, head dim 64
-  if (shape == 4) return launch_fwd_split<64>(p, dropout, f16, stream);
+  if (shape == 4) return launch_fwd_split<64>(p, dropout, f16, tiles.fwd_order != 1, stream);
   if (E == 64) {
     if (shape == 1) return launch_fwd_t<64, 4, 1, 64>(p, causal, dropout, f16, stream);
     if (shape == 2) return launch_fwd_t<64, 2, 2, 64>(p, causal, dropout, f16, stream);

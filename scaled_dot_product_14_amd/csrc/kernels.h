@@ -72,6 +72,7 @@ struct TileChoice {
                   // blocks as two launches (no dropout, no bias; else one launch)
   int bwd_order;  // backward dispatch order: 1 = the arithmetic order that problems past
                   // the order table's size use, whatever the size
+  int fwd_order;  // split forward: 1 = the default workgroup order, no dispatch table
 };
 
 // Tile head dim of the kernels that run head dim E (a multiple of 8, at most 128).

@@ -373,11 +373,14 @@ bool forced_launch_failure(const char* what) {
 // a call without dropout or bias, else it runs one.  SDPA14_BWD_ORDER=1 deals
 // the backward's blocks in the order computed from the block index, which
 // problems of more than 1024 key plus query blocks per head use, at any size.
+// SDPA14_FWD_ORDER=1 runs the causal split forward in its default workgroup
+// order, without the dispatch table that pairs long and short tiles.
 TileChoice tile_choice() {
-  TileChoice t{0, 0, 0};
+  TileChoice t{0, 0, 0, 0};
   if (const char* s = getenv("SDPA14_FWD_SHAPE")) t.fwd_shape = atoi(s);
   if (const char* s = getenv("SDPA14_BWD_ROLES")) t.bwd_roles = atoi(s);
   if (const char* s = getenv("SDPA14_BWD_ORDER")) t.bwd_order = atoi(s);
+  if (const char* s = getenv("SDPA14_FWD_ORDER")) t.fwd_order = atoi(s);
   return t;
 }
 
