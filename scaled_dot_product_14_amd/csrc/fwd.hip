@@ -125,7 +125,7 @@ template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, b
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int n_it_max,
                                          int hold, unsigned char* lds) {
   using G = FwdGeom<E, NQ, NS, BN, BIAS>;
-  constexpr int NW = G::NW, NT = G::NT, BM = G::BM;
+  constexpr int NT = G::NT, BM = G::BM;
   constexpr int NES = E / 16;
   constexpr int NEB = E / 32;
   constexpr int ROWS = G::ROWS, ROW_B = G::ROW_B, KT_B = G::KT_B, STAGE = G::STAGE;
@@ -812,12 +812,14 @@ void plan_split(const FwdParams& p, const SplitRows& r, SplitPlan& plan) {
     };
     // The shorter tile of a pair holds back one sleep unit (~0.3 us) per
     // 32-row step (3 cost units) of estimated length it has less than its
-    // partner; the longer one and the tiles alone start at once.
+    // partner; the longer one and the tiles alone start at once.  Of two
+    // equal tiles one holds a unit, so that the two do not run their phases in
+    // lockstep (0.4% at b2 h12 s1024, where four such pairs per XCD are forced).
     for (int j = 0; j < m; ++j) {
       const Item& a = v[alone + j];   // longest of the paired ...
       const Item& b = v[nx - 1 - j];  // ... with the shortest
       put(j, a, 0);
-      put(C + j, b, std::min(kHoldSteps, (a.cost - b.cost) / 3));
+      put(C + j, b, a.cost == b.cost ? 1 : std::min(kHoldSteps, (a.cost - b.cost) / 3));
     }
     for (int t = 0; t < alone; ++t) put(m + t, v[t], 0);
   }
