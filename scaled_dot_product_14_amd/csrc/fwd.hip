@@ -931,6 +931,12 @@ hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
   // A causal problem that would take two by two, with at least 512 rows and a
   // grid that fits the chip at once, takes the split launch (4): about the
   // last quarter of each head's rows in 32-row, four-share workgroups.
+  // At head dim 64, a causal grid of four-by-one workgroups that runs in one
+  // round is as long as its last tile's walk over the keys; two by two halves
+  // that walk and wins there with dropout or past 1024 rows (8-14%: b4 h16
+  // s1000 p=0.1 32.5 vs 35.6 us, b2 h16 s2048 p=0.1 53.7 vs 62.2 us, b2 h16
+  // s2048 32.9 vs 36.6 us; b4 h16 s1000 without dropout 22.0 vs 21.2 us).
+  // Once four by one needs two rounds or more it stays ahead.
   int shape = tiles.fwd_shape;  // 1: NQ=4,NS=1   2: NQ=2,NS=2   3: NQ=1,NS=4   4: split
   if (shape < 1 || shape > 4) {
     const long wg4 = (long)((p.Sq + 127) / 128) * p.B * p.H;
@@ -938,7 +944,7 @@ hipError_t launch_fwd(const FwdParams& p, bool causal, bool dropout, bool f16,
     if (E == 64 && p.Sk >= 4 * 64 && wg1 <= device_cus())
       shape = 3;
     else if (wg4 >= 512)
-      shape = 1;
+      shape = (E == 64 && causal && wg4 <= 2L * device_cus() && (dropout || p.Sq > 1024)) ? 2 : 1;
     else if (E == 64 && causal && p.Sq >= 512 && split_fits(p))
       shape = 4;
     else
