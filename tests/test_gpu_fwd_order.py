@@ -29,6 +29,8 @@ CASES = [
     (1, 8, 700, 900, 40, "BSHE", 0.0, False, torch.float16),      # per XCD, every tile alone
     (1, 12, 1536, 1536, 64, "BHSE", 0.0, False, torch.bfloat16),  # one entry per workgroup
     (2, 10, 1000, 1000, 64, "BHSE", 0.2, True, torch.float16),    # the same, dropout + bias
+    (2, 16, 832, 832, 64, "BHSE", 0.1, False, torch.bfloat16),    # 512 workgroups: every slot
+    (1, 20, 1280, 1280, 64, "BSHE", 0.0, False, torch.bfloat16),  # 500 of 512, one per workgroup
 ]
 
 
