@@ -767,16 +767,21 @@ void plan_split(const FwdParams& p, const SplitRows& r, SplitPlan& plan) {
     bool heavy;
   };
   auto longer = [](const Item& a, const Item& b) { return a.cost > b.cost; };
+  // Cost of a step: 32-row 3 and 2x2 5 (the traced 0.87-0.9 and 1.2-1.5 us)
+  // when each XCD holds whole heads; 7 and 10 when heads are dealt over the
+  // XCDs (measured 3% faster at b1 h12 s2048 there, 0.3% slower at b2 h12
+  // s1024 in the per-XCD form).
+  const int w32 = bh_count % 8 == 0 ? 3 : 7, w22 = bh_count % 8 == 0 ? 5 : 10;
   static thread_local Item items[kSplitSlots], by_xcd[8][kSplitSlots / 8 + 1];
   int k = 0;
   for (int bh = 0; bh < bh_count; ++bh) {
     for (int rank = 0; rank < r.n_heavy; ++rank) {
       const int qt = r.n_light * 2 + r.n_heavy - 1 - rank;  // in 32-row tiles
-      items[k++] = {3 * steps((qt + 1) * 32, 32, 4), bh, rank, true};
+      items[k++] = {w32 * steps((qt + 1) * 32, 32, 4), bh, rank, true};
     }
     for (int rank = 0; rank < r.n_light; ++rank) {
       const int qt = r.n_light - 1 - rank;
-      items[k++] = {5 * steps((qt + 1) * 64, 64, 2), bh, rank, false};
+      items[k++] = {w22 * steps((qt + 1) * 64, 64, 2), bh, rank, false};
     }
   }
   int cnt[8] = {0};
@@ -817,7 +822,7 @@ void plan_split(const FwdParams& p, const SplitRows& r, SplitPlan& plan) {
       plan.tile[8 * s + x] = {it.heavy, hold, it.bh, it.rank};
     };
     // The shorter tile of a pair holds back one sleep unit (~0.3 us) per
-    // 32-row step (3 cost units) of estimated length it has less than its
+    // 32-row step (w32 cost units) of estimated length it has less than its
     // partner; the longer one and the tiles alone start at once.  Of two
     // equal tiles one holds a unit, so that the two do not run their phases in
     // lockstep (0.4% at b2 h12 s1024, where four such pairs per XCD are forced).
@@ -825,7 +830,7 @@ void plan_split(const FwdParams& p, const SplitRows& r, SplitPlan& plan) {
       const Item& a = v[alone + j];   // longest of the paired ...
       const Item& b = v[nx - 1 - j];  // ... with the shortest
       put(j, a, 0);
-      put(C + j, b, a.cost == b.cost ? 1 : std::min(kHoldSteps, (a.cost - b.cost) / 3));
+      put(C + j, b, a.cost == b.cost ? 1 : std::min(kHoldSteps, (a.cost - b.cost) / w32));
     }
     for (int t = 0; t < alone; ++t) put(m + t, v[t], 0);
   }
