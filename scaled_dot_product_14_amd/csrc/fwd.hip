@@ -123,7 +123,7 @@ struct FwdGeom {
 template <int E, int NQ, int NS, int BN, bool CAUSAL, bool DROPOUT, bool BIAS, bool F16,
           int IGLP = -1>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int n_it_max,
-                                         int hold, unsigned char* lds) {
+                                         int hold, unsigned char* lds, bool split = false) {
   using G = FwdGeom<E, NQ, NS, BN, BIAS>;
   constexpr int NT = G::NT, BM = G::BM;
   constexpr int NES = E / 16;
@@ -289,13 +289,16 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
       }
     }
     if (BIAS && it + 1 < n_it) load_bias(it + 1);
-    // One sub-tile with four 64-key shares (two stages, the workgroup alone
-    // on its CU) issues the next stage at the top of the step, where it is
-    // already free (b2 h3 s1024: 1.5% faster); the other shapes behind the
-    // first products (the split launch's pairs measured 1% slower the other
-    // way).
+    // With two stages the next one is free at the top of the step.  One
+    // sub-tile with four 64-key shares (the workgroup alone on its CU) issues
+    // it there (b2 h3 s1024: 1.5% faster); the split launch's tiles do so from
+    // the second step on, their first step keeping it behind the first
+    // products so that it stays out of the start-up burst (3-6% faster across
+    // the split shapes, 1.2% at b2 h12 s1024; from the first step the headline
+    // was 1.1% slower).  The other shapes keep it behind the first products.
     constexpr bool EARLY = NSTAGE == 2 && NQ == 1 && BN == 64;
-    if ((EARLY || !active) && more) issue(it + NSTAGE - 1);
+    const bool early = EARLY || (NSTAGE == 2 && split && it > 0);
+    if ((early || !active) && more) issue(it + NSTAGE - 1);
     if (active) {
       if constexpr (IGLP >= 0) __builtin_amdgcn_iglp_opt(IGLP);
       const unsigned char* st = stage(it);
@@ -318,7 +321,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
           s[kb] = mfma16<F16>(lds_at<bf16x8>(st, aoff[es] + kb * 32 * ROW_B), qf[es], s[kb]);
       }
       // The next stage's loads go out behind the first products.
-      if (!EARLY && more) issue(it + NSTAGE - 1);
+      if (!early && more) issue(it + NSTAGE - 1);
 
       if (k0 + BN - 1 > (CAUSAL ? min(q0, p.Sk - 1) : p.Sk - 1)) {
         const int lim = key_limit - k0 - 4 * g;  // key offset past which scores are hidden
@@ -656,10 +659,10 @@ __global__ __launch_bounds__(256) void fwd_split_kernel(FwdParams p, int n_heavy
   }
   if (heavy) {
     const int qt = light_rows / 32 + (n_heavy - 1 - rank);
-    fwd_tile<E, 1, 4, 32, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, nmax_h, hold, lds);
+    fwd_tile<E, 1, 4, 32, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, nmax_h, hold, lds, true);
   } else {
     const int qt = n_light - 1 - rank;
-    fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, nmax_l, hold, lds);
+    fwd_tile<E, 2, 2, 64, true, DROPOUT, BIAS, F16, 1>(p, bh, qt, nmax_l, hold, lds, true);
   }
 }
 
