@@ -291,13 +291,15 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
     if (BIAS && it + 1 < n_it) load_bias(it + 1);
     // With two stages the next one is free at the top of the step.  One
     // sub-tile with four 64-key shares (the workgroup alone on its CU) issues
-    // it there (b2 h3 s1024: 1.5% faster); the split launch's tiles do so from
-    // the second step on, their first step keeping it behind the first
-    // products so that it stays out of the start-up burst (3-6% faster across
-    // the split shapes, 1.2% at b2 h12 s1024; from the first step the headline
-    // was 1.1% slower).  The other shapes keep it behind the first products.
+    // it there (b2 h3 s1024: 1.5% faster); the split launch's tiles and four
+    // sub-tiles at head dim 128 do so from the second step on, their first
+    // step keeping it behind the first products so that it stays out of the
+    // start-up burst (3-6% faster across the split shapes, 1.2% at b2 h12
+    // s1024, 2% at b1 h32 q4096 k8192 d128; from the first step the headline
+    // was 1.1% slower).  Two by two keeps it behind the first products (1.5-4%
+    // slower the other way).
     constexpr bool EARLY = NSTAGE == 2 && NQ == 1 && BN == 64;
-    const bool early = EARLY || (NSTAGE == 2 && split && it > 0);
+    const bool early = EARLY || (NSTAGE == 2 && (split || NQ == 4) && it > 0);
     if ((early || !active) && more) issue(it + NSTAGE - 1);
     if (active) {
       if constexpr (IGLP >= 0) __builtin_amdgcn_iglp_opt(IGLP);
