@@ -289,17 +289,15 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
       }
     }
     if (BIAS && it + 1 < n_it) load_bias(it + 1);
-    // With two stages the next one is free at the top of the step.  One
-    // sub-tile with four 64-key shares (the workgroup alone on its CU) issues
-    // it there (b2 h3 s1024: 1.5% faster); the split launch's tiles and four
-    // sub-tiles at head dim 128 do so from the second step on, their first
-    // step keeping it behind the first products so that it stays out of the
-    // start-up burst (3-6% faster across the split shapes, 1.2% at b2 h12
-    // s1024, 2% at b1 h32 q4096 k8192 d128; from the first step the headline
-    // was 1.1% slower).  Two by two keeps it behind the first products (1.5-4%
-    // slower the other way).
-    constexpr bool EARLY = NSTAGE == 2 && NQ == 1 && BN == 64;
-    const bool early = EARLY || (NSTAGE == 2 && (split || NQ == 4) && it > 0);
+    // With two stages the next one is free at the top of the step.  From the
+    // second step on, the split launch's tiles, one sub-tile with four 64-key
+    // shares and four sub-tiles at head dim 128 issue it there; their first
+    // step keeps it behind the first products, out of the start-up burst of
+    // every workgroup (3-6% faster across the split shapes and 1.2% at b2 h12
+    // s1024, 2-2.5% for the other two shapes; from the first step the split
+    // launch was 1.1% slower at b2 h12 s1024).  Two by two keeps it behind the
+    // first products (1.5-4% slower the other way).
+    const bool early = NSTAGE == 2 && (split || NQ == 4 || (NQ == 1 && BN == 64)) && it > 0;
     if ((early || !active) && more) issue(it + NSTAGE - 1);
     if (active) {
       if constexpr (IGLP >= 0) __builtin_amdgcn_iglp_opt(IGLP);
