@@ -296,8 +296,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
     // every workgroup (3-6% faster across the split shapes and 1.2% at b2 h12
     // s1024, 2-2.5% for the other two shapes; from the first step the split
     // launch was 1.1% slower at b2 h12 s1024).  Two by two keeps it behind the
-    // first products (1.5-4% slower the other way).
-    const bool early = NSTAGE == 2 && (split || NQ == 4 || (NQ == 1 && BN == 64)) && it > 0;
+    // first products (1.5-4% slower the other way).  With three stages the
+    // stage two ahead is free at the top of the step too; causal grids issue
+    // it there from the second step on (b4 h16 s1000 and s2048: 2.6% faster),
+    // non-causal ones keep it behind the first products (1.7% slower the
+    // other way at b2 h16 s2048).
+    const bool early =
+        (NSTAGE == 2 ? (split || NQ == 4 || (NQ == 1 && BN == 64)) : CAUSAL) && it > 0;
     if ((early || !active) && more) issue(it + NSTAGE - 1);
     if (active) {
       if constexpr (IGLP >= 0) __builtin_amdgcn_iglp_opt(IGLP);
